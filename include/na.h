@@ -1,0 +1,221 @@
+/*
+ * na.h -- C ABI of the MI355X (gfx950) Generalized Neighborhood Attention
+ * forward library (libna.so).
+ *
+ * Page citations name the pages by title:
+ *   GNA page  = "GNA Sparse Attention Mechanism: Vision-Transformer Compute
+ *               Optimisation in Practice"
+ *   tutorial  = "Video-generation inference speed-up: sparse attention
+ *               configuration tutorial"
+ *   SLA page  = "Sparse attention in video and image generation:
+ *               optimisation practice"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Geometry.  A token grid always has three extents, in (T, H, W) order:
+ *   grid[3], window[3], stride[3].  A 2-D image passes T = 1 (window 1,
+ *   stride 1); a 1-D sequence passes T = H = 1.  Every axis must satisfy
+ *   1 <= stride <= window <= grid, else NA_ERR_INVALID_ARG.
+ *
+ * Which keys a query sees (GNA page, section 1.1).  On each axis the
+ * queries form stride groups g = floor(i / s); the group's leader is its
+ * centre min(g*s + floor(s/2), L-1); the window of every query in the group
+ * starts at clamp(leader - floor(w/2), 0, L - w) and holds w keys.  The
+ * key set of a query is the product of its per-axis windows, so every query
+ * attends exactly prod(window) keys.  s = 1 is sliding-window neighborhood
+ * attention; s > 1 is the block pattern.  No dilation, no causal mask.
+ *
+ * Token layout ("grid order").  q, k, v and out are contiguous
+ *   [batch, T, H, W, heads, head_dim]; lse is [batch, T, H, W, heads].
+ *
+ * Tile layout ("tile order", private to this library, produced by
+ * na_permute).  The grid is cut into boxes of tile[3] tokens (each extent a
+ * power of two); each axis is padded with zeros to a whole number of tiles.
+ * A tile-ordered tensor is [batch, heads, n_tiles, tile_tokens, head_dim]
+ * with tiles and the tokens inside a tile both row-major over (T, H, W).
+ * The "transposed" variant stores every tile as [head_dim, tile_tokens].
+ *
+ * Pointers.  "device" pointers are HIP device memory owned by the caller;
+ * they must be 16-byte aligned.  "host" pointers are ordinary host memory.
+ * The library never frees caller memory.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
+ * stream).  Device entry points only enqueue work: they return before it
+ * runs and do not synchronise.
+ *
+ * Errors.  Every entry point validates its arguments before launching
+ * anything; on failure it returns a negative na_status, launches nothing and
+ * leaves a message for na_last_error().  No entry point throws, prints or
+ * aborts.
+ */
+#ifndef NA_H_
+#define NA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum na_status {
+  NA_OK = 0,
+  NA_ERR_INVALID_ARG = -1,  /* geometry, null/misaligned pointer, sizes      */
+  NA_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, dtype, tiles   */
+  NA_ERR_WORKSPACE = -3,    /* workspace smaller than na_workspace_bytes()   */
+  NA_ERR_HIP = -4           /* the HIP runtime reported an error             */
+} na_status;
+
+typedef enum na_dtype {
+  NA_F32 = 0,       /* fp32 in, fp32 out, fp32 arithmetic throughout       */
+  NA_BF16 = 1,      /* bf16 in/out; fp32 softmax and accumulation          */
+  NA_FP8_E4M3 = 2   /* OCP e4m3fn in with per-tensor scales, bf16 out      */
+} na_dtype;
+
+/* Counts of one tile map, per (batch, head).  "slots" are query-key pairs:
+ * computed_slots = nnz * tile_q_tokens * tile_kv_tokens (what the kernel
+ * multiplies), effective_slots = N * prod(window) (what the method needs). */
+typedef struct na_tilemap_stats {
+  int64_t n_q_tiles;
+  int64_t n_kv_tiles;
+  int64_t nnz;
+  int64_t n_full;
+  int64_t n_boundary;
+  int64_t computed_slots;
+  int64_t effective_slots;
+} na_tilemap_stats;
+
+/* ---------------------------------------------------------------------- */
+/* Host-only entry points (no HIP call; usable without a GPU).            */
+/* ---------------------------------------------------------------------- */
+
+/* Tile shapes the library uses for a problem (GNA page, section 1.2:
+ * decoupled query and key/value tile sizes T_Q and T_KV).  Writes
+ * tile_q[3] and tile_kv[3] (host).  Returns NA_ERR_UNSUPPORTED when no
+ * kernel is built for (head_dim, dtype). */
+na_status na_choose_tiles(const int grid[3], const int window[3],
+                          const int stride[3], int head_dim, na_dtype dtype,
+                          int tile_q[3], int tile_kv[3]);
+
+/* Host tile-map builder (GNA page, section 1.1: the stride decides the
+ * range of KV tiles each Q tile visits; section 2.1: only KV tiles not
+ * fully inside the window need the fine-grained mask).
+ *
+ * Output is CSR over query tiles in row-major tile order:
+ *   qptr[n_q_tiles + 1], kv_idx[nnz] (row-major linear KV-tile index),
+ *   n_full[n_q_tiles].
+ * Inside row a the first n_full[a] entries are *full* tiles (every real
+ * query of the Q tile attends every slot of the KV tile, so the tile has no
+ * padding) and the rest are *boundary* tiles; each part is ascending.
+ * A KV tile is listed iff at least one of its (query, key) pairs is
+ * attended.
+ *
+ * Any of qptr, kv_idx, n_full may be NULL (then only the counts are
+ * produced).  kv_capacity is the length of kv_idx; if it is smaller than
+ * nnz the call returns NA_ERR_INVALID_ARG and writes nothing but *nnz_out
+ * and *stats.  tile extents must be powers of two.  nnz_out and stats may
+ * be NULL. */
+na_status na_build_tile_map(const int grid[3], const int window[3],
+                            const int stride[3], const int tile_q[3],
+                            const int tile_kv[3], int32_t* qptr,
+                            int32_t* kv_idx, int32_t* n_full,
+                            int64_t kv_capacity, int64_t* nnz_out,
+                            na_tilemap_stats* stats);
+
+/* Bytes of device workspace na_forward needs for this problem (the
+ * tile-ordered copies of q, k, v, out and lse).  It grows linearly with the
+ * token count: no N x N buffer exists (tutorial, section 3.3).  Returns 0 if
+ * the arguments are invalid or unsupported (na_last_error() says why). */
+size_t na_workspace_bytes(int batch, int heads, int head_dim,
+                          const int grid[3], const int window[3],
+                          const int stride[3], na_dtype dtype);
+
+/* Message of the last failing call on this thread ("" if none).  Valid
+ * until the next call on the same thread. */
+const char* na_last_error(void);
+
+/* Frees every cached plan (host and device tile maps).  Must not be called
+ * while work that uses a plan may still run on a stream. */
+void na_release_cache(void);
+
+/* ---------------------------------------------------------------------- */
+/* Device entry points (enqueue on `stream`).                             */
+/* ---------------------------------------------------------------------- */
+
+/* One GNA forward pass (GNA page, sections 1.1 and 2.1-2.2):
+ *   permute q, k, v to tile order (zero padding), run the fused tiled
+ *   attention kernel, permute out and lse back to grid order.
+ *
+ * q, k, v  device, [batch, T, H, W, heads, head_dim], dtype `dtype`.
+ * out      device, same shape; fp32 for NA_F32, bf16 for NA_BF16 and
+ *          NA_FP8_E4M3.
+ * lse      device, [batch, T, H, W, heads] fp32, natural-log logsumexp of
+ *          the scaled scores of each query; may be NULL.
+ * scale    multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ * qkv_scale host, 3 floats: dequantisation multipliers of q, k, v for
+ *          NA_FP8_E4M3 (NULL means 1, 1, 1); ignored for other dtypes.
+ * workspace device, caller-owned, >= na_workspace_bytes(...) bytes.
+ * head_dim must be 32 (NA_F32), 64 or 128 (NA_BF16, NA_FP8_E4M3).
+ *
+ * Softmax statistics and accumulation are fp32 in every mode (SLA page,
+ * section 3.1).  The first call for a geometry builds and uploads the tile
+ * map (cached); later calls allocate nothing. */
+na_status na_forward(const void* q, const void* k, const void* v, void* out,
+                     float* lse, int batch, int heads, int head_dim,
+                     const int grid[3], const int window[3],
+                     const int stride[3], float scale, na_dtype dtype,
+                     const float* qkv_scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Token permutation, grid order -> tile order, with zero padding (GNA page,
+ * section 2.2: the permutation before the kernel, fused with padding).
+ *
+ * x   device, [batch, T, H, W, heads, head_dim], elements of elem_bytes
+ *     (1, 2 or 4) bytes.
+ * xt  device, [batch, heads, n_tiles, tile_tokens, head_dim] (transpose=0)
+ *     or [batch, heads, n_tiles, head_dim, tile_tokens] (transpose=1).
+ *     Every element is written, padding slots with zero.
+ * head_dim * elem_bytes must be a multiple of 16. */
+na_status na_permute(const void* x, void* xt, int batch, int heads,
+                     int head_dim, const int grid[3], const int tile[3],
+                     int elem_bytes, int transpose, void* stream);
+
+/* Inverse token permutation, tile order -> grid order, padding dropped
+ * (GNA page, section 2.2: the reverse permutation after the kernel).
+ * xt is [batch, heads, n_tiles, tile_tokens, head_dim]; x is
+ * [batch, T, H, W, heads, head_dim]. */
+na_status na_unpermute(const void* xt, void* x, int batch, int heads,
+                       int head_dim, const int grid[3], const int tile[3],
+                       int elem_bytes, void* stream);
+
+/* Inverse permutation of the logsumexp: lse_t [batch, heads, n_tiles,
+ * tile_tokens] fp32 -> lse [batch, T, H, W, heads] fp32. */
+na_status na_unpermute_lse(const float* lse_t, float* lse, int batch,
+                           int heads, const int grid[3], const int tile[3],
+                           void* stream);
+
+/* The fused attention kernel alone, on tile-ordered tensors (GNA page,
+ * sections 1.1 and 2.1; tutorial, section 3.3: block-wise online softmax).
+ *
+ * qt      device, q in tile order with tile_q tiles.
+ * kt      device, k in tile order with tile_kv tiles.
+ * vt      device, v in *transposed* tile order with tile_kv tiles (fp32 mode:
+ *         plain tile order).
+ * ot      device, [batch, heads, n_q_tiles, tile_q_tokens, head_dim], fp32
+ *         for NA_F32 else bf16; rows of padding queries hold finite values
+ *         that carry no meaning.
+ * lse_t   device, [batch, heads, n_q_tiles, tile_q_tokens] fp32, or NULL.
+ * tile_q/tile_kv must be what na_choose_tiles returns for the problem.
+ * Other arguments as for na_forward. */
+na_status na_attend_tiled(const void* qt, const void* kt, const void* vt,
+                          void* ot, float* lse_t, int batch, int heads,
+                          int head_dim, const int grid[3], const int window[3],
+                          const int stride[3], const int tile_q[3],
+                          const int tile_kv[3], float scale, na_dtype dtype,
+                          const float* qkv_scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NA_H_ */

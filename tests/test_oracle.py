@@ -1,0 +1,332 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against something fixed by the pages or by
+mathematics: values printed on the pages, a hand-derived example, a library
+routine in a case where GNA reduces to it, brute force on tiny inputs,
+closed forms and invariants.  Together they are chosen so that a plausible
+mistake in the oracle (window offset, leader rule, clamp, a dropped scale,
+a transposed operand, a wrong tile split) fails at least one of them.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(1234)
+
+
+def _rand(shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# window geometry
+# ---------------------------------------------------------------------------
+
+def _nearest_window_search(i, L, w):
+    """Independent statement of sliding NA on one axis: among all placements
+    [a, a+w) inside [0, L), take the one whose midpoint is closest to the
+    query, ties going to the placement with more keys before the query."""
+    best = None
+    for a in range(0, L - w + 1):
+        d = abs(a + (w - 1) / 2.0 - i)
+        if best is None or d < best[0] - 1e-12:
+            best = (d, a)
+    return best[1]
+
+
+def test_stride1_window_is_nearest_placement():
+    for L in range(1, 14):
+        for w in range(1, L + 1):
+            for i in range(L):
+                assert oracle.window_start(i, L, w, 1) == _nearest_window_search(i, L, w), (L, w, i)
+
+
+def test_stride_equal_window_gives_disjoint_blocks():
+    # s = w with w | L: the windows tile the axis, query i sees block i // w
+    for L in range(1, 40):
+        for w in range(1, L + 1):
+            if L % w:
+                continue
+            for i in range(L):
+                assert oracle.window_start(i, L, w, w) == (i // w) * w
+
+
+def test_stride_groups_share_one_window_and_jump_by_at_most_s():
+    for L, w, s in [(30, 18, 16), (48, 24, 8), (80, 24, 8), (256, 64, 16), (13, 7, 3), (9, 4, 4)]:
+        st = oracle.window_starts(L, w, s)
+        for i in range(L):
+            assert st[i] == st[(i // s) * s]          # one window per group
+            assert 0 <= st[i] <= L - w                # inside the grid
+        d = np.diff(st)
+        assert (d >= 0).all() and (d <= s).all()      # monotone, jumps <= s
+
+
+def test_worked_1d_example():
+    g = json.load(open(os.path.join(GOLDEN, "worked_1d.json")))
+    val = lambda x: {"ln3": math.log(3), "ln4": math.log(4), "ln6": math.log(6)}.get(x, x)
+    q = np.array([val(x) for x in g["q"]]).reshape(1, 3, 1, 1)
+    k = np.array([val(x) for x in g["k"]]).reshape(1, 3, 1, 1)
+    v = np.array([val(x) for x in g["v"]]).reshape(1, 3, 1, 1)
+    out, lse = oracle.attend(q, k, v, g["grid"], g["window"], g["stride"], g["scale"])
+    np.testing.assert_allclose(out[0, :, 0, 0], g["out"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, :, 0], [val(x) for x in g["lse"]], rtol=0, atol=1e-12)
+
+
+def test_page_sparsity_table():
+    g = json.load(open(os.path.join(GOLDEN, "gna_page_sparsity.json")))
+    for row in g["rows"]:
+        sp = oracle.sparsity(g["grid"], row["window"])
+        assert round(100 * sp, 1) == row["sparsity_percent"]
+
+
+@pytest.mark.parametrize("grid,window,stride", [
+    ((1, 1, 7), (1, 1, 3), (1, 1, 1)),
+    ((1, 5, 6), (1, 3, 4), (1, 2, 3)),
+    ((3, 4, 5), (2, 3, 2), (1, 2, 2)),
+    ((4, 4, 4), (4, 2, 3), (2, 1, 3)),
+])
+def test_key_set_brute_force(grid, window, stride):
+    N = math.prod(grid)
+    W = math.prod(window)
+    table = oracle.key_index_table(grid, window, stride)
+    for qi in range(N):
+        coord = np.unravel_index(qi, grid)
+        ks = oracle.key_set(coord, grid, window, stride)
+        assert len(ks) == W == len(set(ks.tolist()))
+        np.testing.assert_array_equal(table[qi], ks)
+        # membership by brute force over every key of the grid
+        brute = []
+        for kj in range(N):
+            kc = np.unravel_index(kj, grid)
+            ok = all(oracle.window_start(int(c), L, w, s) <= int(x) < oracle.window_start(int(c), L, w, s) + w
+                     for c, x, L, w, s in zip(coord, kc, grid, window, stride))
+            if ok:
+                brute.append(kj)
+        np.testing.assert_array_equal(brute, ks)
+
+
+def test_invalid_geometry_rejected():
+    for g, w, s in [((8,), (9,), (1,)), ((8,), (4,), (5,)), ((8,), (4,), (0,)), ((8,), (0,), (1,))]:
+        with pytest.raises(ValueError):
+            oracle.validate_geometry(g, w, s)
+
+
+# ---------------------------------------------------------------------------
+# attention values
+# ---------------------------------------------------------------------------
+
+def _torch_sdpa64(q, k, v, scale):
+    """Dense fp64 attention by the library routine; q,k,v [B, N, h, D]."""
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)
+    lse = torch.logsumexp(scale * tq @ tk.transpose(-1, -2), dim=-1)
+    return out.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+@pytest.mark.parametrize("grid,stride", [((1, 6, 7), (1, 2, 3)), ((3, 4, 5), (1, 1, 1)), ((2, 3, 4), (2, 3, 2))])
+def test_window_equal_grid_is_dense_attention(grid, stride):
+    B, h, D = 2, 3, 8
+    N = math.prod(grid)
+    q, k, v = (_rand((B, N, h, D)) for _ in range(3))
+    out, lse = oracle.attend(q, k, v, grid, grid, stride, 0.37)
+    ro, rl = _torch_sdpa64(q, k, v, 0.37)
+    np.testing.assert_allclose(out, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("grid,window", [((1, 8, 12), (1, 4, 3)), ((4, 6, 4), (2, 3, 2)), ((1, 1, 30), (1, 1, 5))])
+def test_stride_equal_window_is_block_diagonal_attention(grid, window):
+    B, h, D = 1, 2, 4
+    T, H, W = grid
+    wt, wh, ww = window
+    N = math.prod(grid)
+    q, k, v = (_rand((B, N, h, D)) for _ in range(3))
+    out, lse = oracle.attend(q, k, v, grid, window, window, 0.5)
+
+    def blocks(x):   # [B, N, h, D] -> [B*nblocks, w, h, D]
+        x = x.reshape(B, T // wt, wt, H // wh, wh, W // ww, ww, h, D)
+        x = x.transpose(0, 1, 3, 5, 2, 4, 6, 7, 8)
+        return x.reshape(-1, wt * wh * ww, h, D)
+
+    ro, rl = _torch_sdpa64(blocks(q), blocks(k), blocks(v), 0.5)
+
+    def unblocks(x, last):
+        x = x.reshape(B, T // wt, H // wh, W // ww, wt, wh, ww, h, *last)
+        nd = x.ndim
+        perm = (0, 1, 4, 2, 5, 3, 6) + tuple(range(7, nd))
+        return x.transpose(perm).reshape(B, N, h, *last)
+
+    np.testing.assert_allclose(out, unblocks(ro, (D,)), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, unblocks(rl, ()), rtol=0, atol=1e-12)
+
+
+def test_window_one_returns_v_exactly():
+    grid, B, h, D = (2, 5, 6), 1, 2, 8
+    N = math.prod(grid)
+    q, k, v = (_rand((B, N, h, D)) for _ in range(3))
+    out, lse = oracle.attend(q, k, v, grid, (1, 1, 1), (1, 1, 1), 0.3)
+    assert np.array_equal(out, v)
+    np.testing.assert_allclose(lse, 0.3 * np.einsum("bnhd,bnhd->bnh", q, k), rtol=0, atol=1e-13)
+
+
+def test_zero_query_gives_window_mean():
+    grid, window, stride = (3, 7, 6), (2, 3, 4), (1, 2, 3)
+    B, h, D = 1, 2, 5
+    N, W = math.prod(grid), math.prod(window)
+    q = np.zeros((B, N, h, D))
+    k, v = _rand((B, N, h, D)), _rand((B, N, h, D))
+    out, lse = oracle.attend(q, k, v, grid, window, stride, 1.0)
+    np.testing.assert_allclose(lse, math.log(W), rtol=0, atol=1e-13)
+    for qi in range(N):
+        ks = oracle.key_set(np.unravel_index(qi, grid), grid, window, stride)
+        np.testing.assert_allclose(out[0, qi], v[0, ks].mean(axis=0), rtol=0, atol=1e-13)
+
+
+def test_algebraic_invariants():
+    grid, window, stride = (2, 6, 7), (2, 3, 4), (1, 1, 2)
+    B, h, D = 1, 2, 6
+    N = math.prod(grid)
+    q, k, v = (_rand((B, N, h, D)) for _ in range(3))
+    sc = 0.41
+    out, lse = oracle.attend(q, k, v, grid, window, stride, sc)
+    # constant values -> the constant
+    o2, _ = oracle.attend(q, k, np.full_like(v, 2.5), grid, window, stride, sc)
+    np.testing.assert_allclose(o2, 2.5, rtol=0, atol=1e-13)
+    # k + c*1: output unchanged, lse shifted by scale * <q, c*1>
+    c = 0.7
+    o3, l3 = oracle.attend(q, k + c, v, grid, window, stride, sc)
+    np.testing.assert_allclose(o3, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l3, lse + sc * c * q.sum(-1), rtol=0, atol=1e-12)
+    # affine in v
+    o4, l4 = oracle.attend(q, k, 3.0 * v - 1.25, grid, window, stride, sc)
+    np.testing.assert_allclose(o4, 3.0 * out - 1.25, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l4, lse, rtol=0, atol=0)
+    # the output is a convex combination of the window's values
+    for qi in range(0, N, 5):
+        ks = oracle.key_set(np.unravel_index(qi, grid), grid, window, stride)
+        assert (out[0, qi] <= v[0, ks].max(0) + 1e-12).all()
+        assert (out[0, qi] >= v[0, ks].min(0) - 1e-12).all()
+
+
+def test_translation_equivariance_sliding_mode():
+    # GNA page section 1.1 / 1.2 table: stride 1 keeps translation
+    # equivariance.  Grids A = X[:, :L-d] and B = X[:, d:]; a query whose
+    # window is not shifted by the border in either grid sees the same keys.
+    H, W, w, d = 12, 13, 5, 3
+    B_, h, D = 1, 2, 4
+    X = [_rand((B_, 1, H, W, h, D)) for _ in range(3)]
+    A = [x[:, :, :, : W - d] for x in X]
+    Bt = [x[:, :, :, d:] for x in X]
+    oa, la = oracle.attend(*A, (1, H, W - d), (1, w, w), (1, 1, 1), 0.5)
+    ob, lb = oracle.attend(*Bt, (1, H, W - d), (1, w, w), (1, 1, 1), 0.5)
+    oa = oa.reshape(B_, H, W - d, h, D)
+    ob = ob.reshape(B_, H, W - d, h, D)
+    half = w // 2
+    checked = 0
+    for y in range(H):
+        for x in range(half + d, W - d - half):     # interior of both grids
+            if half <= y < H - half:
+                np.testing.assert_allclose(ob[0, y, x - d], oa[0, y, x], rtol=0, atol=1e-12)
+                checked += 1
+    assert checked > 10
+
+
+def test_block_mode_equivariant_only_for_multiples_of_stride():
+    L, w, s = 40, 8, 4
+    B_, h, D = 1, 1, 3
+    X = [_rand((B_, 1, 1, L, h, D)) for _ in range(3)]
+
+    def run(off, n):
+        return oracle.attend(*[x[:, :, :, off:off + n] for x in X], (1, 1, n), (1, 1, w), (1, 1, s), 1.0)[0]
+
+    n = 28
+    base = run(0, n)
+    shifted = run(s, n)            # shift by a multiple of s: interior agrees
+    np.testing.assert_allclose(shifted[0, 8:16], base[0, 12:20], rtol=0, atol=1e-12)
+    odd = run(1, n)                # shift by 1: the block pattern moves
+    assert not np.allclose(odd[0, 8:16], base[0, 9:17], atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# tile map
+# ---------------------------------------------------------------------------
+
+def _tile_map_nd_brute(grid, window, stride, tq, tk):
+    """Pair counts between every (Q tile, KV tile) by enumerating all N-D
+    (query, key) pairs; same ordering rule as the oracle's CSR."""
+    N = math.prod(grid)
+    nQ = [-(-L // t) for L, t in zip(grid, tq)]
+    nK = [-(-L // t) for L, t in zip(grid, tk)]
+    pairs = {}
+    for qi in range(N):
+        qc = np.unravel_index(qi, grid)
+        a = tuple(int(c) // t for c, t in zip(qc, tq))
+        for kj in oracle.key_set(qc, grid, window, stride):
+            kc = np.unravel_index(int(kj), grid)
+            c = tuple(int(x) // t for x, t in zip(kc, tk))
+            pairs[(a, c)] = pairs.get((a, c), 0) + 1
+    qptr, kv, nfull = [0], [], []
+    for a in itertools.product(*[range(n) for n in nQ]):
+        vq = math.prod(min(t, L - ai * t) for ai, t, L in zip(a, tq, grid))
+        full, bnd = [], []
+        for c in itertools.product(*[range(n) for n in nK]):
+            p = pairs.get((a, c), 0)
+            if p == 0:
+                continue
+            lin = int(np.ravel_multi_index(c, nK))
+            (full if p == vq * math.prod(tk) else bnd).append(lin)
+        kv += sorted(full) + sorted(bnd)
+        nfull.append(len(full))
+        qptr.append(len(kv))
+    return np.array(qptr), np.array(kv), np.array(nfull), sum(pairs.values())
+
+
+@pytest.mark.parametrize("grid,window,stride,tq,tk", [
+    ((1, 9, 11), (1, 5, 4), (1, 1, 2), (1, 4, 4), (1, 2, 4)),
+    ((3, 6, 7), (2, 4, 3), (2, 2, 1), (2, 2, 4), (1, 4, 2)),
+    ((1, 1, 17), (1, 1, 6), (1, 1, 3), (1, 1, 8), (1, 1, 4)),
+    ((4, 8, 8), (4, 4, 4), (4, 4, 4), (2, 4, 4), (2, 4, 4)),
+    ((5, 5, 5), (5, 5, 5), (1, 1, 1), (2, 2, 2), (4, 4, 4)),
+])
+def test_tile_map_against_nd_brute_force(grid, window, stride, tq, tk):
+    qptr, kv, nfull, pr = oracle.tile_map(grid, window, stride, tq, tk, return_pairs=True)
+    bq, bkv, bnf, total = _tile_map_nd_brute(grid, window, stride, tq, tk)
+    np.testing.assert_array_equal(qptr, bq)
+    np.testing.assert_array_equal(kv, bkv)
+    np.testing.assert_array_equal(nfull, bnf)
+    assert pr.sum() == total == math.prod(grid) * math.prod(window)
+
+
+def test_video_block_config_is_perfectly_block_sparse():
+    # GNA page sections 1.1 and 3.1: at 91 % sparsity the speed-up matches the
+    # FLOP reduction, i.e. the KV tiles align with the windows and no
+    # compute is wasted.  With (2,8,8) tiles every listed tile is full.
+    st = oracle.tile_map_stats((30, 48, 80), (18, 24, 24), (16, 8, 8), (2, 8, 8), (2, 8, 8))
+    assert st["n_boundary"] == 0
+    assert st["kv_tiles_per_q_tile"] == 81
+    assert st["efficiency"] == 1.0
+
+
+def test_tile_map_stats_regression():
+    # counts of the workloads' tile maps (regression pins for the host builder)
+    cases = [
+        ((1, 16, 16), (1, 5, 5), (1, 1, 1), (1, 4, 4), (1, 4, 4), 100, 0),
+        ((1, 64, 64), (1, 17, 17), (1, 1, 1), (1, 8, 8), (1, 8, 8), 576, 100),
+        ((1, 64, 64), (1, 16, 16), (1, 8, 8), (1, 8, 8), (1, 4, 4), 1024, 1024),
+        ((30, 48, 80), (30, 40, 40), (1, 1, 1), (2, 8, 8), (2, 8, 8), 432000, 252000),
+        ((1, 256, 256), (1, 64, 64), (1, 16, 16), (1, 16, 16), (1, 8, 8), 16384, 16384),
+    ]
+    for g, w, s, tq, tk, nnz, nfull in cases:
+        st = oracle.tile_map_stats(g, w, s, tq, tk)
+        assert (st["nnz"], st["n_full"]) == (nnz, nfull), g
