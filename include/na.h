@@ -43,6 +43,9 @@
  * stream).  Device entry points only enqueue work: they return before it
  * runs and do not synchronise.
  *
+ * Empty problems.  batch == 0 or heads == 0 is valid: device entry points
+ * then launch nothing and return NA_OK (pointers are not checked).
+ *
  * Errors.  Every entry point validates its arguments before launching
  * anything; on failure it returns a negative na_status, launches nothing and
  * leaves a message for na_last_error().  No entry point throws, prints or
@@ -125,7 +128,8 @@ na_status na_build_tile_map(const int grid[3], const int window[3],
 /* Bytes of device workspace na_forward needs for this problem (the
  * tile-ordered copies of q, k, v, out and lse).  It grows linearly with the
  * token count: no N x N buffer exists (tutorial, section 3.3).  Returns 0 if
- * the arguments are invalid or unsupported (na_last_error() says why). */
+ * the arguments are invalid or unsupported (na_last_error() says why) and
+ * for an empty problem (then na_last_error() is ""). */
 size_t na_workspace_bytes(int batch, int heads, int head_dim,
                           const int grid[3], const int window[3],
                           const int stride[3], na_dtype dtype);

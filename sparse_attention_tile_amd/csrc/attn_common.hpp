@@ -1,0 +1,109 @@
+// Device-side pieces shared by the GNA attention kernels: the kernel
+// argument block, the work-item decode (with the XCD-aware remap) and the
+// per-query window test used on boundary tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace na {
+
+struct KParams {
+  const void* qt;
+  const void* kt;
+  const void* vt;
+  void* ot;
+  float* lse_t;
+  const int32_t* qptr;
+  const int32_t* kv_idx;
+  const int32_t* n_full;
+  int nQ;               // Q tiles per (batch, head)
+  int nK;               // KV tiles per (batch, head)
+  int num_wg;           // batch * heads * nQ
+  int L0, L1, L2;       // grid
+  int w0, w1, w2;       // window
+  int s0, s1, s2;       // stride
+  int lq0, lq1, lq2;    // log2 of the Q tile extents
+  int lk0, lk1, lk2;    // log2 of the KV tile extents
+  int nq0, nq1, nq2;    // Q tiles per axis
+  int nk1, nk2;         // KV tiles along H and W
+  float scale;          // multiplies q.k
+  float c2;             // scale * log2(e)
+  float v_scale;        // multiplies the output (fp8), else 1
+};
+
+inline int host_lg2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+inline KParams make_kparams(const AttnArgs& a) {
+  KParams p;
+  p.qt = a.qt;
+  p.kt = a.kt;
+  p.vt = a.vt;
+  p.ot = a.ot;
+  p.lse_t = a.lse_t;
+  p.qptr = a.qptr;
+  p.kv_idx = a.kv_idx;
+  p.n_full = a.n_full;
+  p.nQ = a.nq[0] * a.nq[1] * a.nq[2];
+  p.nK = a.nk[0] * a.nk[1] * a.nk[2];
+  p.num_wg = a.batch * a.heads * p.nQ;
+  p.L0 = a.L[0]; p.L1 = a.L[1]; p.L2 = a.L[2];
+  p.w0 = a.w[0]; p.w1 = a.w[1]; p.w2 = a.w[2];
+  p.s0 = a.s[0]; p.s1 = a.s[1]; p.s2 = a.s[2];
+  p.lq0 = host_lg2(a.tq[0]); p.lq1 = host_lg2(a.tq[1]); p.lq2 = host_lg2(a.tq[2]);
+  p.lk0 = host_lg2(a.tkv[0]); p.lk1 = host_lg2(a.tkv[1]); p.lk2 = host_lg2(a.tkv[2]);
+  p.nq0 = a.nq[0]; p.nq1 = a.nq[1]; p.nq2 = a.nq[2];
+  p.nk1 = a.nk[1]; p.nk2 = a.nk[2];
+  p.scale = a.scale;
+  p.c2 = a.scale * 1.4426950408889634f;
+  p.v_scale = a.v_scale;
+  return p;
+}
+
+// Window start of query coordinate i on one axis (GNA page, "GNA Sparse
+// Attention Mechanism: Vision-Transformer Compute Optimisation in Practice",
+// section 1.1): queries of a stride group share the window of the group's
+// centre; the window holds floor(w/2) keys before it and stays in the grid.
+__device__ __forceinline__ int dev_window_start(int i, int L, int w, int s) {
+  int lead = (i / s) * s + (s >> 1);
+  lead = lead < L - 1 ? lead : L - 1;
+  int st = lead - (w >> 1);
+  st = st > 0 ? st : 0;
+  return st < L - w ? st : L - w;
+}
+
+// Maps the hardware workgroup id to a work item.  Workgroups are dealt to the
+// 8 XCDs round-robin (id % 8); each XCD has its own L2.  The remap gives
+// every XCD one contiguous range of work items, and inside a (batch, head)
+// the Q tiles are ordered with T fastest, so Q tiles that share the same KV
+// tiles (stride groups along T) run side by side on one XCD.
+struct WorkItem {
+  int bh;      // batch * heads + head
+  int qrow;    // row of the tile map (row-major Q tile index)
+  int a0, a1, a2;  // Q tile coordinates
+};
+
+__device__ __forceinline__ WorkItem decode_work(const KParams& p, int bid) {
+  const int nx = 8;
+  const int q = p.num_wg / nx, r = p.num_wg % nx;
+  const int x = bid % nx, loc = bid / nx;
+  const int logical = x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+  WorkItem w;
+  w.bh = logical / p.nQ;
+  const int t = logical % p.nQ;
+  w.a0 = t % p.nq0;
+  const int rest = t / p.nq0;
+  w.a2 = rest % p.nq2;
+  w.a1 = rest / p.nq2;
+  w.qrow = (w.a0 * p.nq1 + w.a1) * p.nq2 + w.a2;
+  return w;
+}
+
+}  // namespace na

@@ -1,0 +1,48 @@
+// Launchers of the HIP kernels (defined in the .hip files) and the argument
+// block they share.  Host code validates everything before calling these.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+namespace na {
+
+struct AttnArgs {
+  const void* qt;          // q, tile order (tile_q tiles)
+  const void* kt;          // k, tile order (tile_kv tiles)
+  const void* vt;          // v, transposed tile order (tile_kv tiles)
+  void* ot;                // out, tile order (tile_q tiles)
+  float* lse_t;            // lse, tile order, may be null
+  const int32_t* qptr;     // device tile map
+  const int32_t* kv_idx;
+  const int32_t* n_full;
+  int batch, heads, head_dim;
+  int L[3], w[3], s[3];    // grid, window, stride (T, H, W)
+  int tq[3], tkv[3];       // tile extents (powers of two)
+  int nq[3], nk[3];        // tiles per axis
+  float scale;             // multiplies q.k (fp8: includes the q and k scales)
+  float v_scale;           // fp8: multiplies the output; else 1
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t st);
+
+// Kernel shapes the attention launchers accept (host-side check).
+bool attn_bf16_supported(int head_dim, int q_tokens, int kv_tokens);
+bool attn_fp8_supported(int head_dim, int q_tokens, int kv_tokens);
+bool attn_f32_supported(int head_dim, int q_tokens, int kv_tokens);
+
+// LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
+size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);
+
+hipError_t launch_permute(const void* x, void* xt, int batch, int heads, int head_dim,
+                          const int grid[3], const int tile[3], int elem_bytes, int transpose,
+                          hipStream_t st);
+hipError_t launch_unpermute(const void* xt, void* x, int batch, int heads, int head_dim,
+                            const int grid[3], const int tile[3], int elem_bytes, hipStream_t st);
+hipError_t launch_unpermute_lse(const float* lse_t, float* lse, int batch, int heads,
+                                const int grid[3], const int tile[3], hipStream_t st);
+
+}  // namespace na

@@ -1,0 +1,463 @@
+// C ABI of libna.so: argument checks, the plan cache and the launch
+// sequence of one GNA forward pass.  Declarations and their contracts are in
+// include/na.h.
+#include "na.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+
+#include "kernels.hpp"
+#include "tilemap.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+na_status fail(na_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+na::Geometry make_geom(const int grid[3], const int window[3], const int stride[3]) {
+  na::Geometry g;
+  for (int d = 0; d < 3; ++d) {
+    g.L[d] = grid[d];
+    g.w[d] = window[d];
+    g.s[d] = stride[d];
+  }
+  return g;
+}
+
+int elem_bytes(na_dtype dt) {
+  switch (dt) {
+    case NA_F32: return 4;
+    case NA_BF16: return 2;
+    case NA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+int out_bytes(na_dtype dt) { return dt == NA_F32 ? 4 : 2; }
+
+na::Family family(na_dtype dt) {
+  switch (dt) {
+    case NA_F32: return na::Family::F32;
+    case NA_BF16: return na::Family::MFMA16;
+    case NA_FP8_E4M3: return na::Family::FP8;
+  }
+  return na::Family::F32;
+}
+
+bool valid_dtype(int dt) { return dt == NA_F32 || dt == NA_BF16 || dt == NA_FP8_E4M3; }
+
+bool kernel_supported(na_dtype dt, int D, int qtok, int ktok) {
+  switch (dt) {
+    case NA_F32: return na::attn_f32_supported(D, qtok, ktok);
+    case NA_BF16: return na::attn_bf16_supported(D, qtok, ktok);
+    case NA_FP8_E4M3: return na::attn_fp8_supported(D, qtok, ktok);
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// plan cache: host tile map + its device copy, per (device, geometry, tiles)
+// ---------------------------------------------------------------------------
+
+struct Plan {
+  na::TileMap map;
+  int32_t* d_qptr = nullptr;
+  int32_t* d_kv = nullptr;
+  int32_t* d_nfull = nullptr;
+  ~Plan() {
+    if (d_qptr) (void)hipFree(d_qptr);
+    if (d_kv) (void)hipFree(d_kv);
+    if (d_nfull) (void)hipFree(d_nfull);
+  }
+};
+
+using PlanKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int, int, int, int, int, int,
+                           int, int, int>;
+
+std::mutex g_mu;
+std::map<PlanKey, std::unique_ptr<Plan>>& plans() {
+  static auto* m = new std::map<PlanKey, std::unique_ptr<Plan>>();
+  return *m;
+}
+
+na_status get_plan(const na::Geometry& g, const int tq[3], const int tkv[3], Plan** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(NA_ERR_HIP, "hipGetDevice failed");
+  // Test hook: NA_FORCE_MASK=1 marks every listed KV tile as a boundary
+  // tile, so the kernels mask full tiles too (results must not change).
+  const char* fm = std::getenv("NA_FORCE_MASK");
+  const int force_mask = (fm && fm[0] == '1') ? 1 : 0;
+  PlanKey key{dev,      g.L[0],   g.L[1],   g.L[2],   g.w[0], g.w[1], g.w[2],
+              g.s[0],   g.s[1],   g.s[2],   tq[0],  tq[1],  tq[2],
+              tkv[0],   tkv[1],   tkv[2],   force_mask, 0,  0};
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = plans().find(key);
+  if (it != plans().end()) {
+    *out = it->second.get();
+    return NA_OK;
+  }
+  auto p = std::make_unique<Plan>();
+  p->map = na::build_tile_map(g, tq, tkv);
+  if (force_mask) std::fill(p->map.n_full.begin(), p->map.n_full.end(), 0);
+  const size_t nq = p->map.n_full.size();
+  const size_t nnz = p->map.kv_idx.size();
+  if (hipMalloc(&p->d_qptr, (nq + 1) * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc(&p->d_kv, (nnz ? nnz : 1) * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc(&p->d_nfull, nq * sizeof(int32_t)) != hipSuccess)
+    return fail(NA_ERR_HIP, "hipMalloc of the device tile map failed");
+  if (hipMemcpy(p->d_qptr, p->map.qptr.data(), (nq + 1) * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess ||
+      (nnz && hipMemcpy(p->d_kv, p->map.kv_idx.data(), nnz * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) ||
+      hipMemcpy(p->d_nfull, p->map.n_full.data(), nq * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess)
+    return fail(NA_ERR_HIP, "upload of the device tile map failed");
+  *out = p.get();
+  plans()[key] = std::move(p);
+  return NA_OK;
+}
+
+// Test and tuning hook: NA_TILE_Q / NA_TILE_KV="t,h,w" replace the chosen
+// tile shape (the kernel-shape check still applies).  Returns false if the
+// variable is set but malformed.
+bool tile_override(const char* var, int t[3]) {
+  const char* s = std::getenv(var);
+  if (!s || !*s) return true;
+  int v[3];
+  if (std::sscanf(s, "%d,%d,%d", &v[0], &v[1], &v[2]) != 3) return false;
+  if (!na::check_tile(v).empty()) return false;
+  for (int d = 0; d < 3; ++d) t[d] = v[d];
+  return true;
+}
+
+// Sizes of the tile-ordered buffers of one problem.
+struct Layout {
+  int tq[3], tkv[3];
+  int nq[3], nk[3];
+  size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
+  size_t off_q, off_k, off_v, off_o, off_lse, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+na_status check_problem(int batch, int heads, int head_dim, const int grid[3], const int window[3],
+                        const int stride[3], int dtype, Layout* lay) {
+  if (!grid || !window || !stride) return fail(NA_ERR_INVALID_ARG, "grid, window and stride must be non-null");
+  if (batch < 0 || heads < 0) return fail(NA_ERR_INVALID_ARG, "batch and heads must be >= 0");
+  if (!valid_dtype(dtype)) return fail(NA_ERR_INVALID_ARG, "unknown dtype");
+  na::Geometry g = make_geom(grid, window, stride);
+  std::string e = na::check_geometry(g);
+  if (!e.empty()) return fail(NA_ERR_INVALID_ARG, e);
+  const int64_t N = (int64_t)grid[0] * grid[1] * grid[2];
+  if (N > (int64_t(1) << 30)) return fail(NA_ERR_UNSUPPORTED, "more than 2^30 tokens");
+  na_dtype dt = (na_dtype)dtype;
+  if (!na::choose_tiles(g, head_dim, family(dt), lay->tq, lay->tkv))
+    return fail(NA_ERR_UNSUPPORTED, "no kernel for head_dim " + std::to_string(head_dim) + " in this dtype");
+  if (!tile_override("NA_TILE_Q", lay->tq) || !tile_override("NA_TILE_KV", lay->tkv))
+    return fail(NA_ERR_INVALID_ARG, "NA_TILE_Q / NA_TILE_KV must be three powers of two, e.g. 4,8,8");
+  const int qtok = lay->tq[0] * lay->tq[1] * lay->tq[2];
+  const int ktok = lay->tkv[0] * lay->tkv[1] * lay->tkv[2];
+  if (!kernel_supported(dt, head_dim, qtok, ktok))
+    return fail(NA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile combination");
+  int64_t npq = 1, npk = 1;
+  for (int d = 0; d < 3; ++d) {
+    lay->nq[d] = na::ceil_div(grid[d], lay->tq[d]);
+    lay->nk[d] = na::ceil_div(grid[d], lay->tkv[d]);
+    npq *= (int64_t)lay->nq[d] * lay->tq[d];
+    npk *= (int64_t)lay->nk[d] * lay->tkv[d];
+  }
+  const size_t bh = (size_t)batch * heads;
+  const int eb = elem_bytes(dt);
+  lay->q_bytes = bh * npq * head_dim * eb;
+  lay->kv_bytes = bh * npk * head_dim * eb;
+  lay->o_bytes = bh * npq * head_dim * out_bytes(dt);
+  lay->lse_bytes = bh * npq * sizeof(float);
+  lay->off_q = 0;
+  lay->off_k = lay->off_q + round256(lay->q_bytes);
+  lay->off_v = lay->off_k + round256(lay->kv_bytes);
+  lay->off_o = lay->off_v + round256(lay->kv_bytes);
+  lay->off_lse = lay->off_o + round256(lay->o_bytes);
+  lay->total = lay->off_lse + round256(lay->lse_bytes);
+  return NA_OK;
+}
+
+na_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NA_OK;
+  return fail(NA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+na_status check_tile_args(int batch, int heads, int head_dim, const int grid[3], const int tile[3], int eb) {
+  if (!grid || !tile) return fail(NA_ERR_INVALID_ARG, "grid and tile must be non-null");
+  if (batch < 0 || heads < 0 || head_dim < 1) return fail(NA_ERR_INVALID_ARG, "batch, heads >= 0 and head_dim >= 1 needed");
+  for (int d = 0; d < 3; ++d)
+    if (grid[d] < 1) return fail(NA_ERR_INVALID_ARG, "grid extents must be >= 1");
+  std::string e = na::check_tile(tile);
+  if (!e.empty()) return fail(NA_ERR_INVALID_ARG, e);
+  if (eb != 1 && eb != 2 && eb != 4) return fail(NA_ERR_INVALID_ARG, "elem_bytes must be 1, 2 or 4");
+  const int row = head_dim * eb;
+  if (row % 16 != 0 || ((row / 16) & (row / 16 - 1)) != 0)
+    return fail(NA_ERR_UNSUPPORTED, "head_dim * elem_bytes must be 16 times a power of two");
+  const int64_t tt = (int64_t)tile[0] * tile[1] * tile[2];
+  if (tt > 1024) return fail(NA_ERR_UNSUPPORTED, "more than 1024 tokens per tile");
+  return NA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* na_last_error(void) { return g_err.c_str(); }
+
+void na_release_cache(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  plans().clear();
+}
+
+na_status na_choose_tiles(const int grid[3], const int window[3], const int stride[3], int head_dim,
+                          na_dtype dtype, int tile_q[3], int tile_kv[3]) {
+  g_err.clear();
+  if (!tile_q || !tile_kv) return fail(NA_ERR_INVALID_ARG, "tile_q and tile_kv must be non-null");
+  Layout lay;
+  na_status st = check_problem(1, 1, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  for (int d = 0; d < 3; ++d) {
+    tile_q[d] = lay.tq[d];
+    tile_kv[d] = lay.tkv[d];
+  }
+  return NA_OK;
+}
+
+na_status na_build_tile_map(const int grid[3], const int window[3], const int stride[3], const int tile_q[3],
+                            const int tile_kv[3], int32_t* qptr, int32_t* kv_idx, int32_t* n_full,
+                            int64_t kv_capacity, int64_t* nnz_out, na_tilemap_stats* stats) {
+  g_err.clear();
+  if (!grid || !window || !stride || !tile_q || !tile_kv)
+    return fail(NA_ERR_INVALID_ARG, "geometry and tile arrays must be non-null");
+  na::Geometry g = make_geom(grid, window, stride);
+  std::string e = na::check_geometry(g);
+  if (e.empty()) e = na::check_tile(tile_q);
+  if (e.empty()) e = na::check_tile(tile_kv);
+  if (!e.empty()) return fail(NA_ERR_INVALID_ARG, e);
+  na::TileCounts c = na::count_tiles(g, tile_q, tile_kv);
+  if (c.nnz > INT32_MAX || c.n_q_tiles > INT32_MAX)
+    return fail(NA_ERR_UNSUPPORTED, "tile map larger than 2^31 entries");
+  if (nnz_out) *nnz_out = c.nnz;
+  if (stats) {
+    stats->n_q_tiles = c.n_q_tiles;
+    stats->n_kv_tiles = c.n_kv_tiles;
+    stats->nnz = c.nnz;
+    stats->n_full = c.n_full;
+    stats->n_boundary = c.nnz - c.n_full;
+    stats->computed_slots = c.computed_slots;
+    stats->effective_slots = c.effective_slots;
+  }
+  if (!qptr && !kv_idx && !n_full) return NA_OK;
+  if (kv_idx && kv_capacity < c.nnz) return fail(NA_ERR_INVALID_ARG, "kv_capacity smaller than nnz");
+  na::TileMap m = na::build_tile_map(g, tile_q, tile_kv);
+  if (qptr) std::memcpy(qptr, m.qptr.data(), m.qptr.size() * sizeof(int32_t));
+  if (kv_idx && !m.kv_idx.empty()) std::memcpy(kv_idx, m.kv_idx.data(), m.kv_idx.size() * sizeof(int32_t));
+  if (n_full) std::memcpy(n_full, m.n_full.data(), m.n_full.size() * sizeof(int32_t));
+  return NA_OK;
+}
+
+size_t na_workspace_bytes(int batch, int heads, int head_dim, const int grid[3], const int window[3],
+                          const int stride[3], na_dtype dtype) {
+  g_err.clear();
+  Layout lay;
+  if (check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay) != NA_OK) return 0;
+  return lay.total;
+}
+
+na_status na_permute(const void* x, void* xt, int batch, int heads, int head_dim, const int grid[3],
+                     const int tile[3], int elem_bytes, int transpose, void* stream) {
+  g_err.clear();
+  na_status st = check_tile_args(batch, heads, head_dim, grid, tile, elem_bytes);
+  if (st != NA_OK) return st;
+  if (!x || !xt) return fail(NA_ERR_INVALID_ARG, "x and xt must be non-null");
+  if (!aligned16(x) || !aligned16(xt)) return fail(NA_ERR_INVALID_ARG, "x and xt must be 16-byte aligned");
+  if (transpose != 0 && transpose != 1) return fail(NA_ERR_INVALID_ARG, "transpose must be 0 or 1");
+  if (transpose) {
+    const int tt = tile[0] * tile[1] * tile[2];
+    if (tt * elem_bytes % 16 != 0)
+      return fail(NA_ERR_UNSUPPORTED, "transposed tiles need tile_tokens * elem_bytes to be a multiple of 16");
+    if (na::permute_transpose_lds_bytes(head_dim, tt, elem_bytes) > 65536)
+      return fail(NA_ERR_UNSUPPORTED, "transposed tile does not fit in 64 KiB of LDS");
+  }
+  if (batch == 0 || heads == 0) return NA_OK;
+  return hip_status(na::launch_permute(x, xt, batch, heads, head_dim, grid, tile, elem_bytes, transpose,
+                                       (hipStream_t)stream),
+                    "permute launch");
+}
+
+na_status na_unpermute(const void* xt, void* x, int batch, int heads, int head_dim, const int grid[3],
+                       const int tile[3], int elem_bytes, void* stream) {
+  g_err.clear();
+  na_status st = check_tile_args(batch, heads, head_dim, grid, tile, elem_bytes);
+  if (st != NA_OK) return st;
+  if (!x || !xt) return fail(NA_ERR_INVALID_ARG, "x and xt must be non-null");
+  if (!aligned16(x) || !aligned16(xt)) return fail(NA_ERR_INVALID_ARG, "x and xt must be 16-byte aligned");
+  if (batch == 0 || heads == 0) return NA_OK;
+  return hip_status(na::launch_unpermute(xt, x, batch, heads, head_dim, grid, tile, elem_bytes,
+                                         (hipStream_t)stream),
+                    "unpermute launch");
+}
+
+na_status na_unpermute_lse(const float* lse_t, float* lse, int batch, int heads, const int grid[3],
+                           const int tile[3], void* stream) {
+  g_err.clear();
+  na_status st = check_tile_args(batch, heads, 4, grid, tile, 4);
+  if (st != NA_OK) return st;
+  if (!lse_t || !lse) return fail(NA_ERR_INVALID_ARG, "lse_t and lse must be non-null");
+  if ((reinterpret_cast<uintptr_t>(lse_t) & 3u) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(NA_ERR_INVALID_ARG, "lse_t and lse must be 4-byte aligned");
+  if (batch == 0 || heads == 0) return NA_OK;
+  return hip_status(na::launch_unpermute_lse(lse_t, lse, batch, heads, grid, tile, (hipStream_t)stream),
+                    "lse unpermute launch");
+}
+
+static na_status attend_impl(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
+                             int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                             const Layout& lay, float scale, na_dtype dtype, const float* qkv_scale,
+                             hipStream_t stream) {
+  na::Geometry g = make_geom(grid, window, stride);
+  Plan* plan = nullptr;
+  na_status st = get_plan(g, lay.tq, lay.tkv, &plan);
+  if (st != NA_OK) return st;
+  na::AttnArgs a;
+  a.qt = qt;
+  a.kt = kt;
+  a.vt = vt;
+  a.ot = ot;
+  a.lse_t = lse_t;
+  a.qptr = plan->d_qptr;
+  a.kv_idx = plan->d_kv;
+  a.n_full = plan->d_nfull;
+  a.batch = batch;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  for (int d = 0; d < 3; ++d) {
+    a.L[d] = g.L[d];
+    a.w[d] = g.w[d];
+    a.s[d] = g.s[d];
+    a.tq[d] = lay.tq[d];
+    a.tkv[d] = lay.tkv[d];
+    a.nq[d] = lay.nq[d];
+    a.nk[d] = lay.nk[d];
+  }
+  a.scale = scale;
+  a.v_scale = 1.0f;
+  if (dtype == NA_FP8_E4M3 && qkv_scale) {
+    a.scale = scale * qkv_scale[0] * qkv_scale[1];
+    a.v_scale = qkv_scale[2];
+  }
+  hipError_t e = hipSuccess;
+  switch (dtype) {
+    case NA_F32: e = na::launch_attn_f32(a, stream); break;
+    case NA_BF16: e = na::launch_attn_bf16(a, stream); break;
+    case NA_FP8_E4M3: e = na::launch_attn_fp8(a, stream); break;
+  }
+  return hip_status(e, "attention launch");
+}
+
+static na_status check_scales(float scale, na_dtype dtype, const float* qkv_scale) {
+  if (!std::isfinite(scale)) return fail(NA_ERR_INVALID_ARG, "scale must be finite");
+  if (dtype == NA_FP8_E4M3 && qkv_scale) {
+    for (int i = 0; i < 3; ++i)
+      if (!std::isfinite(qkv_scale[i]) || qkv_scale[i] <= 0.f)
+        return fail(NA_ERR_INVALID_ARG, "qkv_scale entries must be finite and > 0");
+  }
+  return NA_OK;
+}
+
+na_status na_attend_tiled(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
+                          int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                          const int tile_q[3], const int tile_kv[3], float scale, na_dtype dtype,
+                          const float* qkv_scale, void* stream) {
+  g_err.clear();
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (!tile_q || !tile_kv) return fail(NA_ERR_INVALID_ARG, "tile_q and tile_kv must be non-null");
+  for (int d = 0; d < 3; ++d)
+    if (tile_q[d] != lay.tq[d] || tile_kv[d] != lay.tkv[d])
+      return fail(NA_ERR_INVALID_ARG, "tile shapes differ from na_choose_tiles()");
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!qt || !kt || !vt || !ot) return fail(NA_ERR_INVALID_ARG, "qt, kt, vt and ot must be non-null");
+  if (!aligned16(qt) || !aligned16(kt) || !aligned16(vt) || !aligned16(ot) || (lse_t && !aligned16(lse_t)))
+    return fail(NA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  st = check_scales(scale, dtype, qkv_scale);
+  if (st != NA_OK) return st;
+  return attend_impl(qt, kt, vt, ot, lse_t, batch, heads, head_dim, grid, window, stride, lay, scale, dtype,
+                     qkv_scale, (hipStream_t)stream);
+}
+
+na_status na_forward(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int heads,
+                     int head_dim, const int grid[3], const int window[3], const int stride[3], float scale,
+                     na_dtype dtype, const float* qkv_scale, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  g_err.clear();
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (batch == 0 || heads == 0) return NA_OK;  // empty problem: nothing to do
+  if (!q || !k || !v || !out) return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (!workspace) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null");
+  if (!aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(lay.total) + " bytes");
+  st = check_scales(scale, dtype, qkv_scale);
+  if (st != NA_OK) return st;
+  if ((head_dim * elem_bytes(dtype)) % 16 != 0 || (head_dim * out_bytes(dtype)) % 16 != 0)
+    return fail(NA_ERR_UNSUPPORTED, "head_dim too small for 16-byte rows");
+  // Make sure the plan exists before anything is enqueued, so a failing
+  // upload leaves the stream untouched.
+  Plan* plan = nullptr;
+  st = get_plan(make_geom(grid, window, stride), lay.tq, lay.tkv, &plan);
+  if (st != NA_OK) return st;
+
+  char* ws = static_cast<char*>(workspace);
+  void* qt = ws + lay.off_q;
+  void* kt = ws + lay.off_k;
+  void* vt = ws + lay.off_v;
+  void* ot = ws + lay.off_o;
+  float* lt = reinterpret_cast<float*>(ws + lay.off_lse);
+  const int eb = elem_bytes(dtype);
+  const int vtrans = dtype == NA_F32 ? 0 : 1;
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = hip_status(na::launch_permute(q, qt, batch, heads, head_dim, grid, lay.tq, eb, 0, s), "permute q")))
+    return st;
+  if ((st = hip_status(na::launch_permute(k, kt, batch, heads, head_dim, grid, lay.tkv, eb, 0, s), "permute k")))
+    return st;
+  if ((st = hip_status(na::launch_permute(v, vt, batch, heads, head_dim, grid, lay.tkv, eb, vtrans, s),
+                       "permute v")))
+    return st;
+  st = attend_impl(qt, kt, vt, ot, lse ? lt : nullptr, batch, heads, head_dim, grid, window, stride, lay, scale,
+                   dtype, qkv_scale, s);
+  if (st != NA_OK) return st;
+  if ((st = hip_status(na::launch_unpermute(ot, out, batch, heads, head_dim, grid, lay.tq, out_bytes(dtype), s),
+                       "unpermute out")))
+    return st;
+  if (lse) {
+    if ((st = hip_status(na::launch_unpermute_lse(lt, lse, batch, heads, grid, lay.tq, s), "unpermute lse")))
+      return st;
+  }
+  return NA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,210 @@
+// Host tile-map builder for GNA.  See tilemap.hpp for the interval rules.
+#include "tilemap.hpp"
+
+#include <algorithm>
+#include <array>
+#include <limits>
+
+namespace na {
+
+int window_start(int i, int L, int w, int s) {
+  // GNA page section 1.1: stride groups share the window of their leader,
+  // the centre of the group; the window holds floor(w/2) keys before the
+  // leader and is shifted to stay inside the grid.
+  const int g = i / s;
+  int lead = g * s + s / 2;
+  if (lead > L - 1) lead = L - 1;
+  int st = lead - w / 2;
+  if (st < 0) st = 0;
+  if (st > L - w) st = L - w;
+  return st;
+}
+
+std::string check_geometry(const Geometry& g) {
+  for (int d = 0; d < 3; ++d) {
+    if (g.L[d] < 1 || g.w[d] < 1 || g.s[d] < 1)
+      return "grid, window and stride must be >= 1 on every axis";
+    if (g.s[d] > g.w[d]) return "stride larger than window on axis " + std::to_string(d);
+    if (g.w[d] > g.L[d]) return "window larger than grid on axis " + std::to_string(d);
+  }
+  return "";
+}
+
+std::string check_tile(const int t[3]) {
+  for (int d = 0; d < 3; ++d) {
+    if (t[d] < 1 || t[d] > 1024 || (t[d] & (t[d] - 1)) != 0)
+      return "tile extents must be powers of two in [1, 1024]";
+  }
+  return "";
+}
+
+std::vector<AxisRange> axis_ranges(int L, int w, int s, int tq, int tkv) {
+  const int nq = ceil_div(L, tq);
+  std::vector<AxisRange> r(nq);
+  for (int a = 0; a < nq; ++a) {
+    const int first = a * tq;
+    const int last = std::min(L, (a + 1) * tq) - 1;
+    const int sf = window_start(first, L, w, s);
+    const int sl = window_start(last, L, w, s);
+    AxisRange x;
+    x.lo = sf / tkv;
+    x.hi = (sl + w - 1) / tkv;
+    // full: c*tkv >= sl, (c+1)*tkv <= sf + w, (c+1)*tkv <= L
+    x.full_lo = ceil_div(sl, tkv);
+    const int top = std::min(sf + w, L);
+    x.full_hi = top / tkv - 1;
+    if (x.full_lo < x.lo) x.full_lo = x.lo;
+    if (x.full_hi > x.hi) x.full_hi = x.hi;
+    r[a] = x;
+  }
+  return r;
+}
+
+TileCounts count_tiles(const Geometry& g, const int tq[3], const int tkv[3]) {
+  TileCounts c;
+  int64_t listed = 1, full = 1, nqt = 1, nkt = 1;
+  for (int d = 0; d < 3; ++d) {
+    auto r = axis_ranges(g.L[d], g.w[d], g.s[d], tq[d], tkv[d]);
+    int64_t sl = 0, sf = 0;
+    for (const auto& x : r) {
+      sl += x.hi - x.lo + 1;
+      sf += std::max(0, x.full_hi - x.full_lo + 1);
+    }
+    listed *= sl;
+    full *= sf;
+    nqt *= (int64_t)r.size();
+    nkt *= ceil_div(g.L[d], tkv[d]);
+  }
+  c.n_q_tiles = nqt;
+  c.n_kv_tiles = nkt;
+  c.nnz = listed;
+  c.n_full = full;
+  const int64_t qtok = (int64_t)tq[0] * tq[1] * tq[2];
+  const int64_t ktok = (int64_t)tkv[0] * tkv[1] * tkv[2];
+  c.computed_slots = listed * qtok * ktok;
+  c.effective_slots = (int64_t)g.L[0] * g.L[1] * g.L[2] * ((int64_t)g.w[0] * g.w[1] * g.w[2]);
+  return c;
+}
+
+TileMap build_tile_map(const Geometry& g, const int tq[3], const int tkv[3]) {
+  TileMap m;
+  std::vector<AxisRange> r[3];
+  for (int d = 0; d < 3; ++d) {
+    r[d] = axis_ranges(g.L[d], g.w[d], g.s[d], tq[d], tkv[d]);
+    m.nq[d] = (int)r[d].size();
+    m.nk[d] = ceil_div(g.L[d], tkv[d]);
+  }
+  m.counts = count_tiles(g, tq, tkv);
+  const int64_t nQ = (int64_t)m.nq[0] * m.nq[1] * m.nq[2];
+  m.qptr.reserve(nQ + 1);
+  m.n_full.reserve(nQ);
+  m.kv_idx.reserve(m.counts.nnz);
+  m.qptr.push_back(0);
+  for (int a0 = 0; a0 < m.nq[0]; ++a0)
+    for (int a1 = 0; a1 < m.nq[1]; ++a1)
+      for (int a2 = 0; a2 < m.nq[2]; ++a2) {
+        const AxisRange& x0 = r[0][a0];
+        const AxisRange& x1 = r[1][a1];
+        const AxisRange& x2 = r[2][a2];
+        // full tiles: product of the full ranges, row-major ascending
+        int nf = 0;
+        for (int c0 = x0.full_lo; c0 <= x0.full_hi; ++c0)
+          for (int c1 = x1.full_lo; c1 <= x1.full_hi; ++c1)
+            for (int c2 = x2.full_lo; c2 <= x2.full_hi; ++c2) {
+              m.kv_idx.push_back((c0 * m.nk[1] + c1) * m.nk[2] + c2);
+              ++nf;
+            }
+        // boundary tiles: the rest of the listed product, ascending
+        for (int c0 = x0.lo; c0 <= x0.hi; ++c0) {
+          const bool f0 = c0 >= x0.full_lo && c0 <= x0.full_hi;
+          for (int c1 = x1.lo; c1 <= x1.hi; ++c1) {
+            const bool f1 = c1 >= x1.full_lo && c1 <= x1.full_hi;
+            for (int c2 = x2.lo; c2 <= x2.hi; ++c2) {
+              const bool f2 = c2 >= x2.full_lo && c2 <= x2.full_hi;
+              if (f0 && f1 && f2) continue;
+              m.kv_idx.push_back((c0 * m.nk[1] + c1) * m.nk[2] + c2);
+            }
+          }
+        }
+        m.n_full.push_back(nf);
+        m.qptr.push_back((int32_t)m.kv_idx.size());
+      }
+  return m;
+}
+
+namespace {
+
+int pow2_ceil(int x) { int p = 1; while (p < x) p <<= 1; return p; }
+
+void shapes_with_product(const Geometry& g, int tokens, std::vector<std::array<int, 3>>& out) {
+  const int cap0 = pow2_ceil(g.L[0]), cap1 = pow2_ceil(g.L[1]), cap2 = pow2_ceil(g.L[2]);
+  for (int a = 1; a <= tokens && a <= cap0; a <<= 1)
+    for (int b = 1; a * b <= tokens && b <= cap1; b <<= 1) {
+      const int c = tokens / (a * b);
+      if (a * b * c != tokens || c > cap2) continue;
+      out.push_back({a, b, c});
+    }
+  if (out.empty()) {
+    // grid smaller than one tile: fill W, then H, then pad along T
+    int rem = tokens;
+    const int c = std::min(rem, cap2);
+    rem /= c;
+    const int b = std::min(rem, cap1);
+    rem /= b;
+    out.push_back({rem, b, c});
+  }
+}
+
+// Relative cost of a (tile_q, tile_kv) pair: computed slots, with a penalty
+// for masked tiles and for the less efficient kernel shapes.
+double tile_cost(const Geometry& g, const int tq[3], const int tkv[3], double q_pen, double kv_pen) {
+  TileCounts c = count_tiles(g, tq, tkv);
+  const double bfrac = c.nnz ? (double)(c.nnz - c.n_full) / (double)c.nnz : 0.0;
+  return (double)c.computed_slots * (1.0 + 0.35 * bfrac) * q_pen * kv_pen;
+}
+
+}  // namespace
+
+bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tkv[3]) {
+  struct Opt { int qtok; double qpen; };
+  struct KOpt { int ktok; double kpen; };
+  std::vector<Opt> qopts;
+  std::vector<KOpt> kopts;
+  switch (fam) {
+    case Family::F32:
+      if (head_dim != 32 && head_dim != 64 && head_dim != 128) return false;
+      qopts = {{64, 1.0}};
+      kopts = {{64, 1.0}};
+      break;
+    case Family::MFMA16:
+    case Family::FP8:
+      if (head_dim != 64 && head_dim != 128) return false;
+      qopts = {{256, 1.0}, {128, 1.3}};
+      kopts = {{128, 1.0}, {64, 1.06}};
+      break;
+  }
+  double best = std::numeric_limits<double>::infinity();
+  bool found = false;
+  for (const auto& qo : qopts) {
+    std::vector<std::array<int, 3>> qs;
+    shapes_with_product(g, qo.qtok, qs);
+    for (const auto& ko : kopts) {
+      std::vector<std::array<int, 3>> ks;
+      shapes_with_product(g, ko.ktok, ks);
+      for (const auto& a : qs)
+        for (const auto& b : ks) {
+          const int q3[3] = {a[0], a[1], a[2]};
+          const int k3[3] = {b[0], b[1], b[2]};
+          const double cost = tile_cost(g, q3, k3, qo.qpen, ko.kpen);
+          if (cost < best) {
+            best = cost;
+            found = true;
+            for (int d = 0; d < 3; ++d) { tq[d] = a[d]; tkv[d] = b[d]; }
+          }
+        }
+    }
+  }
+  return found;
+}
+
+}  // namespace na

@@ -1,0 +1,146 @@
+"""CPU-side checks of libna.so: it loads, exports every declared symbol, its
+host tile-map builder matches the oracle bit for bit, and bad arguments are
+rejected before anything is launched.  No GPU is needed."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "na.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(na_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(na):
+    lib = na.load()
+    declared = _declared_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(na.SYMBOLS)
+
+
+def _cmp_tile_map(na, grid, window, stride, tq, tk):
+    qptr, kv, nf, stats = na.na_build_tile_map(grid, window, stride, tq, tk)
+    oq, okv, onf = oracle.tile_map(grid, window, stride, tq, tk)
+    np.testing.assert_array_equal(qptr, oq)
+    np.testing.assert_array_equal(kv, okv)
+    np.testing.assert_array_equal(nf, onf)
+    os_ = oracle.tile_map_stats(grid, window, stride, tq, tk)
+    assert stats["nnz"] == os_["nnz"] and stats["n_full"] == os_["n_full"]
+    assert stats["computed_slots"] == os_["computed_slots"]
+    assert stats["effective_slots"] == os_["effective_slots"]
+
+
+def test_tile_map_matches_oracle_random_sweep(na):
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        nd = int(rng.integers(1, 4))
+        grid = [1, 1, 1]
+        window = [1, 1, 1]
+        stride = [1, 1, 1]
+        tq = [1, 1, 1]
+        tk = [1, 1, 1]
+        for d in range(3 - nd, 3):
+            L = int(rng.integers(1, 13))
+            w = int(rng.integers(1, L + 1))
+            s = int(rng.integers(1, w + 1))
+            grid[d], window[d], stride[d] = L, w, s
+            tq[d] = int(2 ** rng.integers(0, 4))
+            tk[d] = int(2 ** rng.integers(0, 4))
+        _cmp_tile_map(na, grid, window, stride, tq, tk)
+
+
+@pytest.mark.parametrize("name", ["img16_f32", "img64_sliding", "img64_block", "video_sliding", "video_block",
+                                  "img256_block"])
+def test_tile_map_matches_oracle_on_workloads(na, name):
+    from synth import WORKLOADS
+    wl = WORKLOADS[name]
+    for dt in (na.NA_F32, na.NA_BF16):
+        try:
+            tq, tk = na.na_choose_tiles(wl.grid, wl.window, wl.stride, wl.head_dim, dt)
+        except na.NAError:
+            continue
+        _cmp_tile_map(na, wl.grid, wl.window, wl.stride, tq, tk)
+
+
+def test_chosen_tiles_video_block_are_perfectly_aligned(na):
+    from synth import WORKLOADS
+    wl = WORKLOADS["video_block"]
+    tq, tk = na.na_choose_tiles(wl.grid, wl.window, wl.stride, wl.head_dim, na.NA_BF16)
+    _, _, _, st = na.na_build_tile_map(wl.grid, wl.window, wl.stride, tq, tk)
+    assert st["n_boundary"] == 0
+    assert st["nnz"] == st["n_q_tiles"] * 81
+
+
+def test_workspace_is_linear_in_tokens(na):
+    # no N x N buffer: doubling the grid doubles the workspace (up to padding)
+    a = na.na_workspace_bytes(1, 2, 128, (1, 64, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
+    b = na.na_workspace_bytes(1, 2, 128, (1, 128, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
+    assert 1.9 < b / a < 2.1
+    N = 64 * 64
+    assert a < 8 * N * 2 * 128 * 2 * 4
+
+
+def _status(na, fn, *args):
+    return getattr(na.load(), fn)(*args)
+
+
+def test_invalid_arguments_rejected(na):
+    lib = na.load()
+    I3 = na.I3
+    good = dict(grid=I3(1, 16, 16), window=I3(1, 5, 5), stride=I3(1, 1, 1))
+    ws = na.na_workspace_bytes(1, 1, 64, (1, 16, 16), (1, 5, 5), (1, 1, 1), na.NA_BF16)
+    fake = 1 << 20   # aligned dummy address: never dereferenced, every call below fails first
+
+    def fwd(q=fake, k=fake, v=fake, out=fake, lse=None, B=1, h=1, D=64, grid=None, window=None, stride=None,
+            scale=0.125, dt=na.NA_BF16, ws_ptr=fake, ws_bytes=ws):
+        return lib.na_forward(q, k, v, out, lse, B, h, D, grid or good["grid"], window or good["window"],
+                              stride or good["stride"], scale, dt, None, ws_ptr, ws_bytes, None)
+
+    assert fwd(window=I3(1, 17, 5)) == na.NA_ERR_INVALID_ARG          # window > grid
+    assert fwd(stride=I3(1, 6, 1)) == na.NA_ERR_INVALID_ARG           # stride > window
+    assert fwd(stride=I3(1, 0, 1)) == na.NA_ERR_INVALID_ARG           # stride 0
+    assert fwd(B=-1) == na.NA_ERR_INVALID_ARG
+    assert fwd(B=0, q=None) == na.NA_OK                                # empty problem: nothing launched
+    assert fwd(q=None) == na.NA_ERR_INVALID_ARG                        # null pointer
+    assert fwd(out=fake + 8) == na.NA_ERR_INVALID_ARG                  # misaligned
+    assert fwd(ws_bytes=ws - 1) == na.NA_ERR_WORKSPACE
+    assert fwd(D=48) == na.NA_ERR_UNSUPPORTED
+    assert fwd(dt=7) == na.NA_ERR_INVALID_ARG
+    assert fwd(scale=float("nan")) == na.NA_ERR_INVALID_ARG
+    assert "scale" in na.na_last_error()
+    # permutation kernels
+    assert lib.na_permute(fake, fake, 1, 1, 64, I3(1, 16, 16), I3(1, 3, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_permute(fake, None, 1, 1, 64, I3(1, 16, 16), I3(1, 8, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_permute(fake, fake, 1, 1, 6, I3(1, 16, 16), I3(1, 8, 8), 2, 0, None) == na.NA_ERR_UNSUPPORTED
+    assert lib.na_unpermute(fake, fake, 1, 1, 64, I3(1, 16, 16), I3(1, 8, 8), 3, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_unpermute_lse(fake, None, 1, 1, I3(1, 16, 16), I3(1, 8, 8), None) == na.NA_ERR_INVALID_ARG
+    # tile map capacity
+    nnz = ctypes.c_int64()
+    buf = (ctypes.c_int32 * 4)()
+    qp = (ctypes.c_int32 * 64)()
+    nf = (ctypes.c_int32 * 64)()
+    st = lib.na_build_tile_map(good["grid"], good["window"], good["stride"], I3(1, 4, 4), I3(1, 4, 4),
+                               qp, buf, nf, 4, ctypes.byref(nnz), None)
+    assert st == na.NA_ERR_INVALID_ARG and nnz.value == 100
+    # the workspace query reports invalid problems as 0 bytes
+    assert lib.na_workspace_bytes(1, 1, 64, I3(1, 4, 4), I3(1, 5, 5), I3(1, 1, 1), na.NA_BF16) == 0
+
+
+def test_last_error_is_per_call(na):
+    lib = na.load()
+    lib.na_workspace_bytes(1, 1, 64, na.I3(1, 4, 4), na.I3(1, 5, 5), na.I3(1, 1, 1), na.NA_BF16)
+    assert na.na_last_error() != ""
+    na.na_choose_tiles((1, 16, 16), (1, 5, 5), (1, 1, 1), 64, na.NA_BF16)
+    assert na.na_last_error() == ""

@@ -1,0 +1,84 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on
+seeded inputs.  Small workloads are compared on every output; the full-size
+video and 4K-image workloads on a seeded query sample of a few heads."""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, compare, inputs, run_hip, say
+from synth import WORKLOADS, sample_queries
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["img16_f32", "img64_sliding", "img64_block"])
+def test_small_workloads_all_queries(na, name):
+    wl = WORKLOADS[name]
+    say(f"[parity] {name} grid={wl.grid} w={wl.window} s={wl.stride} D={wl.head_dim} {wl.dtype}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse, _ = run_hip(na, wl, q, k, v, sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    to, tl = TOL[wl.dtype]
+    assert eo <= to and el <= tl
+
+
+@pytest.mark.parametrize("name,heads", [("video_block", (0, 23)), ("video_sliding", (5,)),
+                                        ("img256_block", (0, 17))])
+def test_full_size_sampled(na, name, heads):
+    wl = WORKLOADS[name]
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    tq, _ = na.na_choose_tiles(wl.grid, wl.window, wl.stride, wl.head_dim, na.dtype_code(q.dtype))
+    qs = sample_queries(wl, tq, n_random=256)
+    # keep the oracle to a few seconds: corner/edge tiles are subsampled
+    rng = np.random.default_rng(wl.seed + 11)
+    if len(qs) > 1200:
+        qs = np.unique(np.concatenate([qs[:: max(1, len(qs) // 900)], rng.integers(0, wl.tokens, 256)]))
+    say(f"[parity] {name} full size, tiles {tq}, {len(qs)} sampled queries x heads {heads}")
+    out, lse, _ = run_hip(na, wl, q, k, v, sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse, queries=qs, heads=heads)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    to, tl = TOL[wl.dtype]
+    assert eo <= to and el <= tl
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+
+
+# every attention kernel instantiation: (tile_q, tile_kv) forced through the
+# host tile-override hook; a ragged 3-D grid with boundary and full tiles
+VARIANTS = [
+    ("4,8,8", "2,8,8"), ("2,8,8", "2,8,8"), ("4,8,8", "1,8,8"), ("2,8,8", "1,8,8"),
+    ("1,16,16", "1,8,16"), ("1,8,16", "1,8,8"),
+]
+
+
+@pytest.mark.parametrize("tq,tk", VARIANTS)
+@pytest.mark.parametrize("D", [64, 128])
+def test_kernel_variants_ragged_grid(na, monkeypatch, tq, tk, D):
+    wl = WORKLOADS["video_sliding"].with_(name="ragged", batch=2, heads=3, grid=(5, 19, 27), head_dim=D,
+                                          window=(3, 7, 9), stride=(1, 2, 3), seed=777)
+    monkeypatch.setenv("NA_TILE_Q", tq)
+    monkeypatch.setenv("NA_TILE_KV", tk)
+    say(f"[parity] variant tq={tq} tk={tk} D={D} grid={wl.grid}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse, f = run_hip(na, wl, q, k, v, sc)
+    assert f.tile_q == tuple(int(x) for x in tq.split(","))
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    to, tl = TOL["bf16"]
+    assert eo <= to and el <= tl
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_f32_head_dims(na, D):
+    wl = WORKLOADS["img16_f32"].with_(name="f32d", batch=2, heads=2, grid=(3, 9, 13), head_dim=D,
+                                      window=(2, 5, 4), stride=(1, 2, 1), seed=31 + D)
+    say(f"[parity] f32 D={D} grid={wl.grid}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse, _ = run_hip(na, wl, q, k, v, sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    assert eo <= TOL["f32"][0] and el <= TOL["f32"][1]

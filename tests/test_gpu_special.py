@@ -1,0 +1,165 @@
+"""GPU tests of the permutation kernels and of the method's special cases:
+window 1, zero queries, window = grid, stride = window, translation
+equivariance, masking forced on full tiles, poisoned outputs, empty batch."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import TOL, compare, inputs, run_hip, say
+from synth import WORKLOADS, make_qkv, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _ref_tile_order(x, tile, transpose):
+    """numpy reference of the tile layout: pad, split each axis into
+    (tiles, in-tile), move heads out and the in-tile axes inward."""
+    B, T, H, W, h, D = x.shape
+    tT, tH, tW = tile
+    nT, nH, nW = -(-T // tT), -(-H // tH), -(-W // tW)
+    p = np.zeros((B, nT * tT, nH * tH, nW * tW, h, D), dtype=x.dtype)
+    p[:, :T, :H, :W] = x
+    p = p.reshape(B, nT, tT, nH, tH, nW, tW, h, D).transpose(0, 7, 1, 3, 5, 2, 4, 6, 8)
+    p = p.reshape(B, h, nT * nH * nW, tT * tH * tW, D)
+    return p.transpose(0, 1, 2, 4, 3).copy() if transpose else p
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float8_e4m3fn])
+@pytest.mark.parametrize("tile", [(2, 8, 8), (1, 4, 16), (4, 2, 2)])
+@pytest.mark.parametrize("transpose", [False, True])
+def test_permute_layout_and_round_trip(na, dtype, tile, transpose):
+    if transpose and dtype == torch.float32:
+        pytest.skip("fp32 path keeps V untransposed")
+    D = 64 if dtype != torch.float8_e4m3fn else 128
+    say(f"[permute] {dtype} tile={tile} transpose={transpose}")
+    g = torch.Generator("cpu").manual_seed(5)
+    x = torch.randn((2, 5, 11, 13, 3, D), generator=g).to(dtype)
+    xg = x.cuda()
+    xt = na.permute(xg, tile, transpose=transpose)
+    torch.cuda.synchronize()
+    ib = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float8_e4m3fn: torch.uint8}[dtype]
+    ref = _ref_tile_order(x.view(ib).numpy(), tile, transpose)
+    assert np.array_equal(xt.cpu().view(ib).numpy(), ref)
+    if not transpose:
+        back = na.unpermute(xt, (5, 11, 13), tile)
+        torch.cuda.synchronize()
+        assert torch.equal(back.cpu().view(ib), x.view(ib))
+
+
+def _run(na, wl, q, k, v, window=None, stride=None):
+    f = na.Forward(q, k, v, window or wl.window, stride or wl.stride, scale=wl.scale)
+    out, lse = f()
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_one_returns_v_exactly(na, dtype):
+    wl = WORKLOADS["img64_block"].with_(grid=(3, 17, 20), window=(1, 1, 1), stride=(1, 1, 1), dtype=dtype,
+                                        head_dim=64, heads=2, seed=91)
+    say(f"[special] window 1 {dtype}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse = _run(na, wl, q, k, v)
+    assert torch.equal(out.cpu(), vc)
+    ref = wl.scale * (qc.double() * kc.double()).sum(-1)
+    assert float((lse.cpu().double() - ref).abs().max()) <= TOL[dtype][1]
+
+
+def test_zero_queries_give_window_mean(na):
+    wl = WORKLOADS["img64_block"].with_(grid=(2, 21, 18), window=(2, 6, 5), stride=(1, 3, 2), heads=2, seed=92)
+    say("[special] q = 0")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    qc = torch.zeros_like(qc)
+    out, lse = _run(na, wl, qc.cuda(), k, v)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    assert eo <= TOL["bf16"][0]
+    assert float((lse.cpu().double() - math.log(math.prod(wl.window))).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("stride", [(1, 1, 1), (2, 3, 4)])
+def test_window_equal_grid_is_dense(na, stride):
+    wl = WORKLOADS["img64_block"].with_(grid=(2, 12, 16), window=(2, 12, 16), stride=stride, heads=2,
+                                        head_dim=128, seed=93)
+    say(f"[special] window = grid, stride {stride}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse = _run(na, wl, q, k, v)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  {eo:.3e} {el:.3e}")
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+def test_stride_equal_window_is_block_diagonal(na):
+    wl = WORKLOADS["img64_block"].with_(grid=(4, 24, 32), window=(2, 8, 8), stride=(2, 8, 8), heads=2,
+                                        head_dim=128, seed=94)
+    say("[special] stride = window")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse = _run(na, wl, q, k, v)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+def test_translation_equivariance_sliding(na):
+    # the same tokens seen through two grids shifted by d along W: interior
+    # queries (windows unclamped in both) must agree
+    H, W, w, d = 24, 40, 7, 5
+    g = torch.Generator("cpu").manual_seed(95)
+    X = [torch.randn((1, 1, H, W, 2, 64), generator=g).to(torch.bfloat16) for _ in range(3)]
+    A = [x[:, :, :, : W - d].contiguous().cuda() for x in X]
+    B = [x[:, :, :, d:].contiguous().cuda() for x in X]
+    say("[special] translation equivariance")
+    oa, _ = na.forward(*A, (1, w, w), (1, 1, 1), scale=0.125)
+    ob, _ = na.forward(*B, (1, w, w), (1, 1, 1), scale=0.125)
+    torch.cuda.synchronize()
+    half = w // 2
+    ia = oa[0, 0, half:H - half, half + d:W - d - half].float()
+    ib = ob[0, 0, half:H - half, half:W - 2 * d - half].float()
+    assert ia.numel() > 0
+    assert float((ia - ib).abs().max()) <= 2 * TOL["bf16"][0]
+
+
+def test_forced_mask_on_full_tiles_is_bit_identical(na, monkeypatch):
+    # GNA page section 2.1: the mask is only needed on boundary tiles; applying
+    # it to full tiles too must not change a single bit
+    wl = WORKLOADS["video_block"].with_(grid=(20, 24, 32), heads=2, seed=96)
+    say("[special] forced mask")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out1, lse1 = _run(na, wl, q, k, v)
+    monkeypatch.setenv("NA_FORCE_MASK", "1")
+    out2, lse2 = _run(na, wl, q, k, v)
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_every_output_written(na):
+    wl = WORKLOADS["video_sliding"].with_(grid=(3, 13, 21), window=(3, 5, 7), heads=3, seed=97)
+    say("[special] poisoned outputs")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale)
+    f.out.fill_(float("nan"))
+    f.lse.fill_(float("nan"))
+    f.workspace.fill_(0xFF)   # NaN patterns in every tile-order buffer
+    out, lse = f()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+def test_no_lse_and_empty_batch(na):
+    wl = WORKLOADS["img64_sliding"].with_(heads=2, seed=98)
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    say("[special] lse = NULL, empty batch")
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, return_lse=False)
+    out, lse = f()
+    torch.cuda.synchronize()
+    assert lse is None
+    f2 = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale)
+    out2, _ = f2()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    e = torch.empty((0, 1, 64, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
+    o, l = na.forward(e, e, e, (1, 17, 17), (1, 1, 1))
+    assert o.shape == e.shape and l.shape == e.shape[:-1]
