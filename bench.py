@@ -1,0 +1,264 @@
+"""Benchmark of the GNA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video_block]
+
+One step = one complete forward (na_forward: permute q, k, v to tile order,
+the fused attention kernel, permute out and lse back) over one batch of
+seeded synthetic input that is already resident in HBM.  The default
+workload is the 91 %-sparse 3-D video configuration (batch 1, 24 heads,
+30x48x80 tokens, head_dim 128, window 18x24x24, stride 16x8x8, bf16).
+
+Prints ONE JSON line: effective TFLOP/s (only unmasked QK^T + PV FLOPs,
+4 * b * h * N * prod(window) * D per call) of the whole forward, ms per step,
+the per-stage times measured with HIP events on the launch stream, the
+roofline of the attention kernel, the dense full-window speed-up reference
+and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense MFMA / fp32 vector
+HBM_GBPS = 8000.0
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def time_steps(torch, fn, steps, warmup):
+    """Runs fn warmup times untimed, then `steps` times between HIP events on
+    the current stream; returns per-step ms and total ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = _events(torch, steps + 1)
+    ev[0].record()
+    for i in range(steps):
+        fn()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return per, ev[0].elapsed_time(ev[steps])
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("attn_bf16.hip", "attn_common.hpp"):
+        with open(os.path.join(ROOT, "sparse_attention_tile_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, src_hash):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_bf16_video_block_traffic.json")
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != src_hash or d.get("workload") != workload:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, sc, budget_s=15.0):
+    """The CPU oracle (as it stands) on a bounded sample: random queries of
+    head 0, grown until about `budget_s` seconds of CPU work."""
+    import numpy as np
+
+    import oracle
+    from synth import to_f64
+
+    qh = to_f64(q[..., 0:1, :], sc[0])
+    kh = to_f64(k[..., 0:1, :], sc[1])
+    vh = to_f64(v[..., 0:1, :], sc[2])
+    rng = np.random.default_rng(wl.seed + 7)
+    W = wl.keys_per_query
+    done_q, wall, cpu = 0, 0.0, 0.0
+    n = 8
+    while wall < budget_s:
+        qs = rng.integers(0, wl.tokens, n)
+        c0, t0 = time.process_time(), time.perf_counter()
+        oracle.attend(qh, kh, vh, wl.grid, wl.window, wl.stride, wl.scale, queries=qs)
+        wall += time.perf_counter() - t0
+        cpu += time.process_time() - c0
+        done_q += n
+        n = min(n * 2, 512)
+    flops = 4.0 * done_q * W * wl.head_dim
+    return {
+        "value": flops / wall / 1e12,
+        "unit": "TFLOP/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{done_q} random queries of head 0 (of {wl.batch * wl.heads * wl.tokens} query rows), "
+                  f"{wall:.1f} s wall; value = effective FLOPs of the sample / wall time",
+        "ms_per_call_extrapolated": wall * 1e3 * (wl.batch * wl.heads * wl.tokens) / done_q,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="video_block")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the GNA forward is "
+              "independent per (batch, head) and is not run across GPUs here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 30, "launches": 3}))
+        return
+
+    import sparse_attention_tile_amd as na
+    from synth import WORKLOADS, make_qkv
+
+    wl = WORKLOADS[args.workload]
+    qc, kc, vc, sc = make_qkv(wl, device="cpu")
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+    fp8 = wl.dtype == "fp8"
+    fwd = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, qkv_scale=sc if fp8 else None)
+    dcode = fwd.dtype
+    eff = wl.effective_flops
+
+    # ---- the timed region: K complete forward passes
+    torch.cuda.synchronize()
+    per, total = time_steps(torch, fwd, args.steps, args.warmup)
+    ms = total / args.steps
+    med = statistics.median(per)
+    std = statistics.pstdev(per)
+
+    # ---- stages, each timed with HIP events on the launch stream
+    stream = torch.cuda.current_stream().cuda_stream
+    tq, tk = fwd.tile_q, fwd.tile_kv
+    eb = q.element_size()
+    qt = na.permute(q, tq)
+    kt = na.permute(k, tk)
+    vt = na.permute(v, tk, transpose=(dcode != na.NA_F32))
+    out_dtype = torch.float32 if dcode == na.NA_F32 else torch.bfloat16
+    ot = torch.empty(qt.shape, dtype=out_dtype, device="cuda")
+    lt = torch.empty(qt.shape[:-1], dtype=torch.float32, device="cuda")
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+
+    def attn():
+        na.na_attend_tiled(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), ot.data_ptr(), lt.data_ptr(), B, H, D,
+                           wl.grid, wl.window, wl.stride, tq, tk, wl.scale, dcode, sc if fp8 else None, stream)
+
+    def perm_qkv():
+        na.na_permute(q.data_ptr(), qt.data_ptr(), B, H, D, wl.grid, tq, eb, 0, stream)
+        na.na_permute(k.data_ptr(), kt.data_ptr(), B, H, D, wl.grid, tk, eb, 0, stream)
+        na.na_permute(v.data_ptr(), vt.data_ptr(), B, H, D, wl.grid, tk, eb, int(dcode != na.NA_F32), stream)
+
+    def unperm():
+        na.na_unpermute(ot.data_ptr(), fwd.out.data_ptr(), B, H, D, wl.grid, tq, ot.element_size(), stream)
+        na.na_unpermute_lse(lt.data_ptr(), fwd.lse.data_ptr(), B, H, wl.grid, tq, stream)
+
+    st_steps = max(5, args.steps)
+    a_per, a_tot = time_steps(torch, attn, st_steps, 2)
+    attn_ms = a_tot / st_steps
+    p_per, p_tot = time_steps(torch, perm_qkv, st_steps, 2)
+    perm_ms = p_tot / st_steps
+    u_per, u_tot = time_steps(torch, unperm, st_steps, 2)
+    unperm_ms = u_tot / st_steps
+    perm_bytes = q.numel() * eb * 3 + (qt.numel() + kt.numel() + vt.numel()) * eb
+    unperm_bytes = ot.numel() * ot.element_size() + fwd.out.numel() * fwd.out.element_size() + \
+        lt.numel() * 4 + fwd.lse.numel() * 4
+
+    _, _, _, tstats = na.na_build_tile_map(wl.grid, wl.window, wl.stride, tq, tk)
+    computed = 4.0 * B * H * tstats["computed_slots"] * D
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = eff / (attn_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(wl.name, src_hash)
+
+    result = {
+        "metric": "effective TFLOP/s (unmasked FLOPs) of one GNA forward, 1 MI355X",
+        "value": eff / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3", "f32": "f32"}[wl.dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: batch {B}, {H} heads, grid {'x'.join(map(str, wl.grid))}, head_dim {D}, "
+                        f"window {'x'.join(map(str, wl.window))}, stride {'x'.join(map(str, wl.stride))}, "
+                        f"{wl.dtype}, N(0,1) inputs",
+            "effective_flops": eff,
+            "sparsity": 1.0 - wl.keys_per_query / wl.tokens,
+            "tile_q": list(tq), "tile_kv": list(tk),
+        },
+        "pct_of_peak": 100.0 * (eff / (ms * 1e-3) / 1e12) / peak,
+        "step_ms_median": med,
+        "step_ms_std_over_median": std / med,
+        "stages_ms": {"permute_qkv": perm_ms, "attention": attn_ms, "unpermute_out_lse": unperm_ms},
+        "permute_GBps": perm_bytes / (perm_ms * 1e-3) / 1e9,
+        "unpermute_GBps": unperm_bytes / (unperm_ms * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "attn_bf16_kernel" if dcode == na.NA_BF16 else "attention",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic,
+            "computed_over_effective_flops": computed / eff,
+            "kernel_source_sha256_16": src_hash,
+        },
+    }
+
+    if not args.no_dense and wl.name == "video_block":
+        dwl = WORKLOADS["video_dense"]
+        dfwd = na.Forward(q, k, v, dwl.window, dwl.stride, scale=dwl.scale)
+        _, dtot = time_steps(torch, dfwd, 3, 1)
+        dms = dtot / 3
+        result["dense_reference"] = {
+            "workload": "same tensors, window = grid (dense attention)",
+            "ms": dms,
+            "effective_TFLOPs": dwl.effective_flops / (dms * 1e-3) / 1e12,
+            "speedup_vs_dense": dms / ms,
+            "flop_ratio": dwl.effective_flops / eff,
+        }
+        del dfwd
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, qc, kc, vc, sc)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -155,7 +155,8 @@ void na_release_cache(void);
  *          NA_FP8_E4M3.
  * lse      device, [batch, T, H, W, heads] fp32, natural-log logsumexp of
  *          the scaled scores of each query; may be NULL.
- * scale    multiplies q.k before the softmax (usually 1/sqrt(head_dim)).
+ * scale    multiplies q.k before the softmax (usually 1/sqrt(head_dim));
+ *          finite and >= 0 (a negative factor belongs in q).
  * qkv_scale host, 3 floats: dequantisation multipliers of q, k, v for
  *          NA_FP8_E4M3 (NULL means 1, 1, 1); ignored for other dtypes.
  * workspace device, caller-owned, >= na_workspace_bytes(...) bytes.

@@ -12,9 +12,11 @@
 // lse = m + ln l.
 //
 // gfx950 mapping
-// * Workgroup = 4 wavefronts (one per SIMD), Q tile = 4 * QB * 32 queries;
-//   each wave owns QB blocks of 32 queries and keeps its Q operand in
-//   registers for the whole kernel.
+// * Two wavefronts per SIMD, 32 queries per wavefront, NW wavefronts per
+//   workgroup (Q tile = 32 NW queries).  While one wave of a SIMD runs its
+//   softmax on the VALU, the other keeps the matrix core busy; each wave
+//   holds its Q operand in registers for the whole kernel and its O
+//   accumulators in the accumulation registers.
 // * The transposed products are used: S^T = K Q^T and O^T = V^T P^T on
 //   v_mfma_f32_32x32x16_bf16.  In the C layout of S^T a lane holds one query
 //   and 16 keys, so the row max needs one cross-half exchange
@@ -29,6 +31,10 @@
 //   j is multiplied.  A 16-byte-chunk XOR swizzle, applied through the
 //   per-lane global addresses of those loads, keeps the MFMA operand reads
 //   free of LDS bank conflicts.
+// * Lazy rescaling: the running max only moves when a block max exceeds it
+//   by more than 2^8 (after exp2), so O is rescaled almost never after the
+//   first block; P stays <= 256.  Results equal exact-max softmax up to
+//   rounding.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -40,10 +46,11 @@ namespace na {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-// 16-byte chunk swizzle of a tile row with `cpr` chunks.
+// 16-byte chunk swizzle of a tile row with CPR chunks.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (CPR >= 16) return row & 15;
@@ -64,30 +71,38 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Copies one tile (ROWS rows of ROWB bytes) global -> LDS, swizzled.  Each
-// wave moves 1 KiB per instruction: lane i fills LDS bytes [16 i, 16 i + 16)
-// of the wave's segment, so its global address picks the chunk that belongs
-// there.
-template <int ROWB, int TILEB>
-__device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g, lds_u8* lds, int wv, int lane) {
+// Global -> LDS copy of one tile (rows of ROWB bytes), swizzled.  Each wave
+// moves 1 KiB per instruction: lane i fills LDS bytes [16 i, 16 i + 16) of
+// the wave's segment, so its global address picks the chunk that belongs
+// there.  Wave wv copies segments wv, wv + NW, ...; segment NW i + wv starts
+// 1024 NW i bytes after segment wv and the swizzle repeats within that
+// distance, so a lane's source offset is lane_off + 1024 NW i with lane_off
+// fixed for the whole kernel.
+template <int ROWB, int NW>
+__device__ __forceinline__ int dma_lane_offset(int wv, int lane) {
   constexpr int CPR = ROWB / 16;
-  constexpr int SEGS = TILEB / 1024;
-  static_assert(SEGS % 4 == 0, "tile must split evenly over 4 waves");
-#pragma unroll
-  for (int i = 0; i < SEGS / 4; ++i) {
-    const int seg = i * 4 + wv;
-    const int byte = seg * 1024 + lane * 16;
-    const int row = byte / ROWB;
-    const int pc = (byte % ROWB) / 16;
-    const int lc = pc ^ swz<CPR>(row);
-    __builtin_amdgcn_global_load_lds(g + row * ROWB + lc * 16, (__attribute__((address_space(3))) void*)(lds + seg * 1024),
-                                     16, 0, 0);
-  }
+  constexpr int ROUND = 1024 * NW;
+  static_assert(ROUND % ROWB == 0, "rows must divide the copy round");
+  static_assert((ROUND / ROWB) % 16 == 0, "swizzle period must divide the copy round");
+  const int byte = wv * 1024 + lane * 16;
+  const int row = byte / ROWB;
+  const int pc = (byte % ROWB) / 16;
+  return row * ROWB + ((pc ^ swz<CPR>(row)) * 16);
 }
 
-template <int D, int QB, int KVT>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
-  constexpr int QT = 4 * QB * 32;        // queries per workgroup
+template <int TILEB, int NW>
+__device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds, int wv) {
+  constexpr int ROUND = 1024 * NW;
+  static_assert(TILEB % ROUND == 0, "tile must split evenly over the waves");
+#pragma unroll
+  for (int i = 0; i < TILEB / ROUND; ++i)
+    __builtin_amdgcn_global_load_lds(g + i * ROUND + lane_off,
+                                     (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0, 0);
+}
+
+template <int D, int NW, int KVT>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
+  constexpr int QT = NW * 32;            // queries per workgroup
   constexpr int DC = D / 16;             // k-steps of S^T
   constexpr int DB = D / 32;             // 32-row blocks of O^T
   constexpr int KB = KVT / 32;           // 32-key blocks per KV tile
@@ -102,34 +117,30 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
   const int lane = tid & 63, wv = tid >> 6, hh = lane >> 5, lq = lane & 31;
   const WorkItem wi = decode_work(p, blockIdx.x);
   const size_t qtile = (size_t)wi.bh * p.nQ + wi.qrow;
+  const int row = wv * 32 + lq;          // this lane's query inside the Q tile
 
   // ---- Q operand (B of S^T = K Q^T): query = lane % 32, 8 dims per lane
-  const __bf16* qbase = static_cast<const __bf16*>(p.qt) + qtile * QT * D;
-  bf16x8 qr[QB][DC];
-  int st0[QB], st1[QB], st2[QB];
+  bf16x8 qr[DC];
+  {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.qt) + (qtile * QT + row) * D);
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const int row = wv * QB * 32 + b * 32 + lq;
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(qbase + (size_t)row * D);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) qr[b][c] = src[2 * c + hh];
+    for (int c = 0; c < DC; ++c) qr[c] = src[2 * c + hh];
+  }
+  // this query's window on each axis (for boundary tiles)
+  int st0, st1, st2;
+  {
     const int px = row & ((1 << p.lq2) - 1);
     const int py = (row >> p.lq2) & ((1 << p.lq1) - 1);
     const int pt = row >> (p.lq1 + p.lq2);
-    st0[b] = dev_window_start((wi.a0 << p.lq0) + pt, p.L0, p.w0, p.s0);
-    st1[b] = dev_window_start((wi.a1 << p.lq1) + py, p.L1, p.w1, p.s1);
-    st2[b] = dev_window_start((wi.a2 << p.lq2) + px, p.L2, p.w2, p.s2);
+    st0 = dev_window_start((wi.a0 << p.lq0) + pt, p.L0, p.w0, p.s0);
+    st1 = dev_window_start((wi.a1 << p.lq1) + py, p.L1, p.w1, p.s1);
+    st2 = dev_window_start((wi.a2 << p.lq2) + px, p.L2, p.w2, p.s2);
   }
 
-  f32x16 o[QB][DB];
-  float m[QB], l[QB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    m[b] = -INFINITY;
-    l[b] = 0.f;
-#pragma unroll
-    for (int d = 0; d < DB; ++d) o[b][d] = f32x16{};
-  }
+  for (int d = 0; d < DB; ++d) o[d] = f32x16{};
+  float m = -INFINITY, l = 0.f;
 
   const int beg = p.qptr[wi.qrow], end = p.qptr[wi.qrow + 1];
   const int nfull = p.n_full[wi.qrow];
@@ -137,11 +148,20 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
   const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * TILEB;
   const float c2 = p.c2;
   const int km2 = (1 << p.lk2) - 1, km1 = (1 << p.lk1) - 1, ksh = p.lk1 + p.lk2;
+  static_assert(KVT / 16 <= 8, "validity mask holds 64 bits");
+  const int koff = dma_lane_offset<KROW, NW>(wv, lane);
+  const int voff = dma_lane_offset<VROW, NW>(wv, lane);
+  // the reference max moves only when a block max exceeds it by 8 / c2
+  const float thr = c2 > 0.f ? 8.f / c2 : 3.0e38f;
+  // K row this lane feeds to the MFMA, and its swizzle (same in every block)
+  const int krow0 = kperm(lq);
+  const int kswz = swz<KROW / 16>(krow0);
+  const int vswz = swz<VROW / 16>(lq);
 
   {  // prologue: first tile in flight
     const int kv = p.kv_idx[beg];
-    tile_to_lds<KROW, TILEB>(kbase + (size_t)kv * TILEB, lds, wv, lane);
-    tile_to_lds<VROW, TILEB>(vbase + (size_t)kv * TILEB, lds + TILEB, wv, lane);
+    tile_to_lds<TILEB, NW>(kbase + (size_t)kv * TILEB, koff, lds, wv);
+    tile_to_lds<TILEB, NW>(vbase + (size_t)kv * TILEB, voff, lds + TILEB, wv);
   }
 
   for (int j = beg; j < end; ++j) {
@@ -151,121 +171,112 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
     if (j + 1 < end) {
       const int kv = p.kv_idx[j + 1];
       lds_u8* nb = lds + (stage ^ 1) * STAGE;
-      tile_to_lds<KROW, TILEB>(kbase + (size_t)kv * TILEB, nb, wv, lane);
-      tile_to_lds<VROW, TILEB>(vbase + (size_t)kv * TILEB, nb + TILEB, wv, lane);
+      tile_to_lds<TILEB, NW>(kbase + (size_t)kv * TILEB, koff, nb, wv);
+      tile_to_lds<TILEB, NW>(vbase + (size_t)kv * TILEB, voff, nb + TILEB, wv);
     }
     const unsigned char* Ks = smem + stage * STAGE;
     const unsigned char* Vs = Ks + TILEB;
     const bool boundary = (j - beg) >= nfull;
-    int k0 = 0, k1 = 0, k2 = 0;
+    // Boundary tile: one validity bit per key this lane holds.  The lane's
+    // keys come in groups of 8 consecutive tile slots (g = 2 gg + hh); the
+    // KV tile's W extent is >= 8, so a group shares its (T, H) position and
+    // covers 8 consecutive W positions.  Bit 8 gg + t <-> slot 8 g + t, which
+    // is accumulator i = 16 kb + ... of block kb (see below).
+    uint64_t vmask = 0;
     if (boundary) {
       const int kv = p.kv_idx[j];
-      k2 = (kv % p.nk2) << p.lk2;
-      k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
-      k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+      const int k2 = (kv % p.nk2) << p.lk2;
+      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+#pragma unroll 1
+      for (int gg = 0; gg < KVT / 16; ++gg) {
+        const int r0 = 8 * (2 * gg + hh);
+        const int lo = min(max(st2 - k2 - (r0 & km2), 0), 8);
+        const int hi = min(max(st2 + p.w2 - k2 - (r0 & km2), 0), 8);
+        unsigned bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+        const bool th = ((unsigned)(k0 + (r0 >> ksh) - st0) < (unsigned)p.w0) &
+                        ((unsigned)(k1 + ((r0 >> p.lk2) & km1) - st1) < (unsigned)p.w1);
+        vmask |= (uint64_t)(th ? bits : 0u) << (8 * gg);
+      }
     }
 
-#pragma unroll 1
-    for (int kb = 0; kb < KB; ++kb) {
-      // ---- S^T block: 32 keys x 32 queries per query block
-      f32x16 s[QB];
 #pragma unroll
-      for (int b = 0; b < QB; ++b) s[b] = f32x16{};
-      const int krow = kb * 32 + kperm(lq);
+    for (int kb = 0; kb < KB; ++kb) {
+      // ---- S^T block: 32 keys x 32 queries
+      f32x16 s = f32x16{};
+      const unsigned char* krowp = Ks + (kb * 32 + krow0) * KROW;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        const int pc = (2 * c + hh) ^ swz<KROW / 16>(krow);
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + krow * KROW + pc * 16);
-#pragma unroll
-        for (int b = 0; b < QB; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[b][c], s[b], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krowp + (((2 * c + hh) ^ kswz) * 16));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[c], s, 0, 0, 0);
       }
 
       // ---- online softmax (fp32); accumulator i <-> key 16*(i/8) + 8*hh + i%8
-      bf16x8 pv[QB][2];
+      if (boundary) {
+        // accumulator i is slot 32 kb + 16 (i/8) + 8 hh + i%8: group gg = 2 kb + i/8
+        const unsigned mb = (unsigned)(vmask >> (16 * kb)) & 0xFFFFu;
 #pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        if (boundary) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = kb * 32 + 16 * (i >> 3) + 8 * hh + (i & 7);
-            const int kx = k2 + (r & km2);
-            const int ky = k1 + ((r >> p.lk2) & km1);
-            const int kt = k0 + (r >> ksh);
-            const bool ok = (unsigned)(kt - st0[b]) < (unsigned)p.w0 &&
-                            (unsigned)(ky - st1[b]) < (unsigned)p.w1 &&
-                            (unsigned)(kx - st2[b]) < (unsigned)p.w2;
-            if (!ok) s[b][i] = -INFINITY;
-          }
-        }
-        float bm = s[b][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) bm = fmaxf(bm, s[b][i]);
-        bm = xhalf_max(bm);
-        const float mn = fmaxf(m[b], bm);
-        const float ref = mn == -INFINITY ? 0.f : mn;  // every key so far masked
-        const float alpha = __builtin_amdgcn_exp2f((m[b] - ref) * c2);
-        const float nref = -ref * c2;
-        float rs = 0.f;
-        float pf[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pf[i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], c2, nref));
-          rs += pf[i];
-        }
-        l[b] = l[b] * alpha + rs;
-        m[b] = mn;
-#pragma unroll
-        for (int d = 0; d < DB; ++d) o[b][d] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[b][0][i] = (__bf16)pf[i];
-          pv[b][1][i] = (__bf16)pf[8 + i];
-        }
+        for (int i = 0; i < 16; ++i) s[i] = ((mb >> i) & 1u) ? s[i] : -INFINITY;
       }
+      float bm = fmaxf(s[0], s[1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) bm = fmaxf(bm, fmaxf(s[i], s[i + 1]));
+      bm = xhalf_max(bm);
+      if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {  // rare after the first block
+        const float mn = fmaxf(m, bm);
+        // alpha = 0 while nothing was accumulated (O and l are still 0)
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        m = mn;
+      }
+      const float nref = m == -INFINITY ? 0.f : -m * c2;   // every key so far masked: p = 0
+      bf16x8 pv[2];
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nref));
+        rs += e;
+        pv[i >> 3][i & 7] = (__bf16)e;
+      }
+      l += rs;
 
       // ---- O^T += V^T P^T over the block's two 16-key halves
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          const int vr = d * 32 + lq;
-          const int pc = (4 * kb + 2 * c + hh) ^ swz<VROW / 16>(vr);
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + vr * VROW + pc * 16);
-#pragma unroll
-          for (int b = 0; b < QB; ++b) o[b][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[b][c], o[b][d], 0, 0, 0);
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(Vs + (d * 32 + lq) * VROW + (((4 * kb + 2 * c + hh) ^ vswz) * 16));
+          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[c], o[d], 0, 0, 0);
         }
       }
     }
   }
 
   // ---- epilogue: O / l in bf16, lse = m*scale + ln l
-  __bf16* obase = static_cast<__bf16*>(p.ot) + qtile * QT * D;
+  const float lt = xhalf_sum(l);
+  const float inv = 1.f / lt;
+  __bf16* orow = static_cast<__bf16*>(p.ot) + (qtile * QT + row) * D;
 #pragma unroll
-  for (int b = 0; b < QB; ++b) {
-    const float lt = xhalf_sum(l[b]);
-    const float inv = 1.f / lt;
-    const int row = wv * QB * 32 + b * 32 + lq;
+  for (int d = 0; d < DB; ++d) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-        bf16x4 v;
-        v[0] = (__bf16)(o[b][d][4 * g + 0] * inv);
-        v[1] = (__bf16)(o[b][d][4 * g + 1] * inv);
-        v[2] = (__bf16)(o[b][d][4 * g + 2] * inv);
-        v[3] = (__bf16)(o[b][d][4 * g + 3] * inv);
-        const int col = d * 32 + 8 * g + 4 * hh;
-        *reinterpret_cast<bf16x4*>(obase + (size_t)row * D + col) = v;
-      }
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+      v[0] = (__bf16)(o[d][4 * g + 0] * inv);
+      v[1] = (__bf16)(o[d][4 * g + 1] * inv);
+      v[2] = (__bf16)(o[d][4 * g + 2] * inv);
+      v[3] = (__bf16)(o[d][4 * g + 3] * inv);
+      *reinterpret_cast<bf16x4*>(orow + d * 32 + 8 * g + 4 * hh) = v;
     }
-    if (p.lse_t && hh == 0) p.lse_t[qtile * QT + row] = m[b] * p.scale + logf(lt);
   }
+  if (p.lse_t && hh == 0) p.lse_t[qtile * QT + row] = (m == -INFINITY ? 0.f : m * p.scale) + logf(lt);
 }
 
-template <int D, int QB, int KVT>
+template <int D, int NW, int KVT>
 hipError_t launch_cfg(const KParams& p, hipStream_t st) {
-  attn_bf16_kernel<D, QB, KVT><<<p.num_wg, 256, 0, st>>>(p);
+  attn_bf16_kernel<D, NW, KVT><<<p.num_wg, NW * 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -276,21 +287,24 @@ bool attn_bf16_supported(int head_dim, int q_tokens, int kv_tokens) {
          (kv_tokens == 64 || kv_tokens == 128);
 }
 
+// Extra shape rule of the boundary mask: the KV tile's W extent is >= 8.
+bool attn_bf16_tile_ok(const int tile_kv[3]) { return tile_kv[2] >= 8; }
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const KParams p = make_kparams(a);
   const int qtok = a.tq[0] * a.tq[1] * a.tq[2];
   const int ktok = a.tkv[0] * a.tkv[1] * a.tkv[2];
+  if (!attn_bf16_supported(a.head_dim, qtok, ktok) || !attn_bf16_tile_ok(a.tkv)) return hipErrorInvalidValue;
   const int key = (a.head_dim == 128 ? 4 : 0) | (qtok == 256 ? 2 : 0) | (ktok == 128 ? 1 : 0);
-  if (!attn_bf16_supported(a.head_dim, qtok, ktok)) return hipErrorInvalidValue;
   switch (key) {
-    case 0: return launch_cfg<64, 1, 64>(p, st);
-    case 1: return launch_cfg<64, 1, 128>(p, st);
-    case 2: return launch_cfg<64, 2, 64>(p, st);
-    case 3: return launch_cfg<64, 2, 128>(p, st);
-    case 4: return launch_cfg<128, 1, 64>(p, st);
-    case 5: return launch_cfg<128, 1, 128>(p, st);
-    case 6: return launch_cfg<128, 2, 64>(p, st);
-    default: return launch_cfg<128, 2, 128>(p, st);
+    case 0: return launch_cfg<64, 4, 64>(p, st);
+    case 1: return launch_cfg<64, 4, 128>(p, st);
+    case 2: return launch_cfg<64, 8, 64>(p, st);
+    case 3: return launch_cfg<64, 8, 128>(p, st);
+    case 4: return launch_cfg<128, 4, 64>(p, st);
+    case 5: return launch_cfg<128, 4, 128>(p, st);
+    case 6: return launch_cfg<128, 8, 64>(p, st);
+    default: return launch_cfg<128, 8, 128>(p, st);
   }
 }
 

@@ -33,6 +33,8 @@ hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t st);
 bool attn_bf16_supported(int head_dim, int q_tokens, int kv_tokens);
 bool attn_fp8_supported(int head_dim, int q_tokens, int kv_tokens);
 bool attn_f32_supported(int head_dim, int q_tokens, int kv_tokens);
+// The bf16/fp8 kernels need KV tiles at least 8 tokens wide along W.
+bool attn_bf16_tile_ok(const int tile_kv[3]);
 
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
 size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);

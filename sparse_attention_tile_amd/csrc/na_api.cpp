@@ -170,7 +170,7 @@ na_status check_problem(int batch, int heads, int head_dim, const int grid[3], c
     return fail(NA_ERR_INVALID_ARG, "NA_TILE_Q / NA_TILE_KV must be three powers of two, e.g. 4,8,8");
   const int qtok = lay->tq[0] * lay->tq[1] * lay->tq[2];
   const int ktok = lay->tkv[0] * lay->tkv[1] * lay->tkv[2];
-  if (!kernel_supported(dt, head_dim, qtok, ktok))
+  if (!kernel_supported(dt, head_dim, qtok, ktok) || (dt != NA_F32 && !na::attn_bf16_tile_ok(lay->tkv)))
     return fail(NA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile combination");
   int64_t npq = 1, npk = 1;
   for (int d = 0; d < 3; ++d) {
@@ -373,7 +373,8 @@ static na_status attend_impl(const void* qt, const void* kt, const void* vt, voi
 }
 
 static na_status check_scales(float scale, na_dtype dtype, const float* qkv_scale) {
-  if (!std::isfinite(scale)) return fail(NA_ERR_INVALID_ARG, "scale must be finite");
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(NA_ERR_INVALID_ARG, "scale must be finite and >= 0 (fold a sign into q)");
   if (dtype == NA_FP8_E4M3 && qkv_scale) {
     for (int i = 0; i < 3; ++i)
       if (!std::isfinite(qkv_scale[i]) || qkv_scale[i] <= 0.f)

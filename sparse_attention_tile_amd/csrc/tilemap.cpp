@@ -136,12 +136,14 @@ namespace {
 
 int pow2_ceil(int x) { int p = 1; while (p < x) p <<= 1; return p; }
 
-void shapes_with_product(const Geometry& g, int tokens, std::vector<std::array<int, 3>>& out) {
-  const int cap0 = pow2_ceil(g.L[0]), cap1 = pow2_ceil(g.L[1]), cap2 = pow2_ceil(g.L[2]);
+// Power-of-two tile shapes with `tokens` tokens, each extent at most the
+// grid extent rounded up to a power of two, and the W extent >= min_w.
+void shapes_with_product(const Geometry& g, int tokens, std::vector<std::array<int, 3>>& out, int min_w) {
+  const int cap0 = pow2_ceil(g.L[0]), cap1 = pow2_ceil(g.L[1]), cap2 = std::max(pow2_ceil(g.L[2]), min_w);
   for (int a = 1; a <= tokens && a <= cap0; a <<= 1)
     for (int b = 1; a * b <= tokens && b <= cap1; b <<= 1) {
       const int c = tokens / (a * b);
-      if (a * b * c != tokens || c > cap2) continue;
+      if (a * b * c != tokens || c > cap2 || c < min_w) continue;
       out.push_back({a, b, c});
     }
   if (out.empty()) {
@@ -170,6 +172,7 @@ bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tk
   struct KOpt { int ktok; double kpen; };
   std::vector<Opt> qopts;
   std::vector<KOpt> kopts;
+  int min_kv_w = 1;
   switch (fam) {
     case Family::F32:
       if (head_dim != 32 && head_dim != 64 && head_dim != 128) return false;
@@ -181,16 +184,17 @@ bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tk
       if (head_dim != 64 && head_dim != 128) return false;
       qopts = {{256, 1.0}, {128, 1.3}};
       kopts = {{128, 1.0}, {64, 1.06}};
+      min_kv_w = 8;   // the boundary mask works on 8-key groups along W
       break;
   }
   double best = std::numeric_limits<double>::infinity();
   bool found = false;
   for (const auto& qo : qopts) {
     std::vector<std::array<int, 3>> qs;
-    shapes_with_product(g, qo.qtok, qs);
+    shapes_with_product(g, qo.qtok, qs, 1);
     for (const auto& ko : kopts) {
       std::vector<std::array<int, 3>> ks;
-      shapes_with_product(g, ko.ktok, ks);
+      shapes_with_product(g, ko.ktok, ks, min_kv_w);
       for (const auto& a : qs)
         for (const auto& b : ks) {
           const int q3[3] = {a[0], a[1], a[2]};

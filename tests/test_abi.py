@@ -119,6 +119,7 @@ def test_invalid_arguments_rejected(na):
     assert fwd(D=48) == na.NA_ERR_UNSUPPORTED
     assert fwd(dt=7) == na.NA_ERR_INVALID_ARG
     assert fwd(scale=float("nan")) == na.NA_ERR_INVALID_ARG
+    assert fwd(scale=-0.5) == na.NA_ERR_INVALID_ARG
     assert "scale" in na.na_last_error()
     # permutation kernels
     assert lib.na_permute(fake, fake, 1, 1, 64, I3(1, 16, 16), I3(1, 3, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG
