@@ -15,7 +15,8 @@ import math
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libna.so")
+# NA_LIB may name another build of the same library (e.g. to compare builds)
+LIB_PATH = os.environ.get("NA_LIB") or os.path.join(HERE, "libna.so")
 
 NA_OK, NA_ERR_INVALID_ARG, NA_ERR_UNSUPPORTED, NA_ERR_WORKSPACE, NA_ERR_HIP = 0, -1, -2, -3, -4
 NA_F32, NA_BF16, NA_FP8_E4M3 = 0, 1, 2

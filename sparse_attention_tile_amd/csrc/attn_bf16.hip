@@ -39,6 +39,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn_common.hpp"
 
@@ -47,6 +48,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -100,6 +102,66 @@ __device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g,
                                      (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0, 0);
 }
 
+// The rounds of a tile copy that belong to step kb of KB: the copy of the
+// next tile is spread over the current tile's key blocks, so the CU's vector
+// memory path sees a steady trickle instead of every wave's whole copy at
+// the barrier (which would stall all waves until the address queue drains).
+template <int TILEB, int NW, int KB>
+__device__ __forceinline__ void tile_to_lds_step(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds,
+                                                 int wv, int kb) {
+  constexpr int ROUND = 1024 * NW;
+  constexpr int ROUNDS = TILEB / ROUND;
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i)
+    if ((i * KB) / ROUNDS == kb)
+      __builtin_amdgcn_global_load_lds(g + i * ROUND + lane_off,
+                                       (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0,
+                                       0);
+}
+
+// S^T block kb (32 keys x 32 queries) of the K tile at Ks.
+template <int D, int KROW>
+__device__ __forceinline__ f32x16 qk_block(const unsigned char* Ks, int kb, int krow0, int kswz, int hh,
+                                           const bf16x8* qr) {
+  f32x16 s = f32x16{};
+  const unsigned char* krowp = Ks + (kb * 32 + krow0) * KROW;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(krowp + (((2 * c + hh) ^ kswz) * 16));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[c], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// Boundary tiles: accumulator i of block kb is key slot 32 kb + 16 (i/8) +
+// 8 hh + i%8, whose validity is bit 16 kb + i of the lane's mask.
+__device__ __forceinline__ void apply_mask(f32x16& s, uint64_t vmask, int kb) {
+  const unsigned mb = (unsigned)(vmask >> (16 * kb)) & 0xFFFFu;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = ((mb >> i) & 1u) ? s[i] : -INFINITY;
+}
+
+// Lazy rescaling: move the reference max m only when the block max exceeds
+// it by more than thr (= 8 / c2, a factor 2^8 after exp2); then scale l and
+// O by exp2((m_old - m_new) c2).  The branch is wave-uniform and rare.
+template <int DB>
+__device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, float& l, f32x16 (&o)[DB], float c2,
+                                                  float thr) {
+  float bm = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) bm = fmaxf(bm, fmaxf(s[i], s[i + 1]));
+  bm = xhalf_max(bm);
+  if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {
+    const float mn = fmaxf(m, bm);
+    // alpha = 0 while nothing was accumulated (O and l are still 0)
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+    l *= alpha;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) o[d] *= alpha;
+    m = mn;
+  }
+}
+
 template <int D, int NW, int KVT>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   constexpr int QT = NW * 32;            // queries per workgroup
@@ -126,15 +188,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
 #pragma unroll
     for (int c = 0; c < DC; ++c) qr[c] = src[2 * c + hh];
   }
-  // this query's window on each axis (for boundary tiles)
+  // this query's window on each axis (for boundary tiles), and whether the
+  // wave holds any real query: a wave whose 32 slots are all padding (ragged
+  // grid edge) skips the arithmetic and only helps with the tile copies
   int st0, st1, st2;
+  bool wave_active;
   {
     const int px = row & ((1 << p.lq2) - 1);
     const int py = (row >> p.lq2) & ((1 << p.lq1) - 1);
     const int pt = row >> (p.lq1 + p.lq2);
-    st0 = dev_window_start((wi.a0 << p.lq0) + pt, p.L0, p.w0, p.s0);
-    st1 = dev_window_start((wi.a1 << p.lq1) + py, p.L1, p.w1, p.s1);
-    st2 = dev_window_start((wi.a2 << p.lq2) + px, p.L2, p.w2, p.s2);
+    const int gt = (wi.a0 << p.lq0) + pt, gy = (wi.a1 << p.lq1) + py, gx = (wi.a2 << p.lq2) + px;
+    st0 = dev_window_start(gt, p.L0, p.w0, p.s0);
+    st1 = dev_window_start(gy, p.L1, p.w1, p.s1);
+    st2 = dev_window_start(gx, p.L2, p.w2, p.s2);
+    wave_active = __builtin_amdgcn_ballot_w64(gt < p.L0 && gy < p.L1 && gx < p.L2) != 0;
   }
 
   f32x16 o[DB];
@@ -142,8 +209,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
   float m = -INFINITY, l = 0.f;
 
-  const int beg = p.qptr[wi.qrow], end = p.qptr[wi.qrow + 1];
-  const int nfull = p.n_full[wi.qrow];
+  // The tile map is read-only for the whole launch: read it through the
+  // constant address space so the loads are scalar (s_load, lgkmcnt) and never
+  // wait on the vector-memory counter the K/V DMA uses.
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  cint* qptr = (cint*)p.qptr;
+  cint* kv_idx = (cint*)p.kv_idx;
+  const int qrow_u = __builtin_amdgcn_readfirstlane(wi.qrow);
+  const int beg = __builtin_amdgcn_readfirstlane(qptr[qrow_u]);
+  const int end = __builtin_amdgcn_readfirstlane(qptr[qrow_u + 1]);
+  const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u]);
   const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (size_t)wi.bh * p.nK * TILEB;
   const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * TILEB;
   const float c2 = p.c2;
@@ -158,90 +233,48 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const int kswz = swz<KROW / 16>(krow0);
   const int vswz = swz<VROW / 16>(lq);
 
-  {  // prologue: first tile in flight
-    const int kv = p.kv_idx[beg];
-    tile_to_lds<TILEB, NW>(kbase + (size_t)kv * TILEB, koff, lds, wv);
-    tile_to_lds<TILEB, NW>(vbase + (size_t)kv * TILEB, voff, lds + TILEB, wv);
-  }
+  // KV-tile indices live in scalar registers: kv_cur is tile j, kv_nxt tile
+  // j+1; tile j+2's index is fetched one tile ahead so no wait on it ever
+  // sits between a barrier and the next tile's DMA.
+  int kv_cur = kv_idx[beg];
+  int kv_nxt = beg + 1 < end ? kv_idx[beg + 1] : 0;
+  tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);   // prologue: tile 0 in flight
+  tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
 
-  for (int j = beg; j < end; ++j) {
-    const int stage = (j - beg) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < end) {
-      const int kv = p.kv_idx[j + 1];
-      lds_u8* nb = lds + (stage ^ 1) * STAGE;
-      tile_to_lds<TILEB, NW>(kbase + (size_t)kv * TILEB, koff, nb, wv);
-      tile_to_lds<TILEB, NW>(vbase + (size_t)kv * TILEB, voff, nb + TILEB, wv);
-    }
-    const unsigned char* Ks = smem + stage * STAGE;
-    const unsigned char* Vs = Ks + TILEB;
-    const bool boundary = (j - beg) >= nfull;
-    // Boundary tile: one validity bit per key this lane holds.  The lane's
-    // keys come in groups of 8 consecutive tile slots (g = 2 gg + hh); the
-    // KV tile's W extent is >= 8, so a group shares its (T, H) position and
-    // covers 8 consecutive W positions.  Bit 8 gg + t <-> slot 8 g + t, which
-    // is accumulator i = 16 kb + ... of block kb (see below).
-    uint64_t vmask = 0;
-    if (boundary) {
-      const int kv = p.kv_idx[j];
-      const int k2 = (kv % p.nk2) << p.lk2;
-      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
-      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
-#pragma unroll 1
-      for (int gg = 0; gg < KVT / 16; ++gg) {
-        const int r0 = 8 * (2 * gg + hh);
-        const int lo = min(max(st2 - k2 - (r0 & km2), 0), 8);
-        const int hi = min(max(st2 + p.w2 - k2 - (r0 & km2), 0), 8);
-        unsigned bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
-        const bool th = ((unsigned)(k0 + (r0 >> ksh) - st0) < (unsigned)p.w0) &
-                        ((unsigned)(k1 + ((r0 >> p.lk2) & km1) - st1) < (unsigned)p.w1);
-        vmask |= (uint64_t)(th ? bits : 0u) << (8 * gg);
-      }
-    }
-
+  // One KV tile from LDS: a software pipeline over its 32-key blocks.  S^T of
+  // block kb+1 is issued before the exponentials of block kb, and the max /
+  // rescale decision of block kb+1 comes after the P V product of block kb, so
+  // each step offers the scheduler independent MFMA and VALU work.  BOUNDARY
+  // tiles apply the key-validity mask; full tiles have no mask code at all.
+  // copy of the next tile, issued step by step inside tile_body
+  const unsigned char* nk = kbase;
+  const unsigned char* nv = vbase;
+  lds_u8* nbuf = lds;
+  auto tile_body = [&](const unsigned char* Ks, const unsigned char* Vs, uint64_t vmask, auto bnd) {
+    constexpr bool BOUNDARY = decltype(bnd)::value;
+    f32x16 s = qk_block<D, KROW>(Ks, 0, krow0, kswz, hh, qr);
+    if constexpr (BOUNDARY) apply_mask(s, vmask, 0);
+    rescale_if_needed(s, m, l, o, c2, thr);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      // ---- S^T block: 32 keys x 32 queries
-      f32x16 s = f32x16{};
-      const unsigned char* krowp = Ks + (kb * 32 + krow0) * KROW;
-#pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krowp + (((2 * c + hh) ^ kswz) * 16));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[c], s, 0, 0, 0);
-      }
-
-      // ---- online softmax (fp32); accumulator i <-> key 16*(i/8) + 8*hh + i%8
-      if (boundary) {
-        // accumulator i is slot 32 kb + 16 (i/8) + 8 hh + i%8: group gg = 2 kb + i/8
-        const unsigned mb = (unsigned)(vmask >> (16 * kb)) & 0xFFFFu;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = ((mb >> i) & 1u) ? s[i] : -INFINITY;
-      }
-      float bm = fmaxf(s[0], s[1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) bm = fmaxf(bm, fmaxf(s[i], s[i + 1]));
-      bm = xhalf_max(bm);
-      if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {  // rare after the first block
-        const float mn = fmaxf(m, bm);
-        // alpha = 0 while nothing was accumulated (O and l are still 0)
-        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < DB; ++d) o[d] *= alpha;
-        m = mn;
-      }
+      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
+      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
+      f32x16 sn;
+      if (kb + 1 < KB) sn = qk_block<D, KROW>(Ks, kb + 1, krow0, kswz, hh, qr);
+      // ---- P = exp2(S c2 - m c2) in bf16; accumulator i <-> key 16*(i/8) + 8*hh + i%8
       const float nref = m == -INFINITY ? 0.f : -m * c2;   // every key so far masked: p = 0
       bf16x8 pv[2];
-      float rs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c2, nref));
-        rs += e;
-        pv[i >> 3][i & 7] = (__bf16)e;
+      for (int i = 0; i < 16; ++i) pv[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[i], c2, nref));
+      // row sum of the bf16 weights the P V product uses (two dot2 chains)
+      const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+      float ra = 0.f, rb = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ra = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[0][2 * q], pv[0][2 * q + 1]}, one2, ra, false);
+        rb = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pv[1][2 * q], pv[1][2 * q + 1]}, one2, rb, false);
       }
-      l += rs;
-
+      l += ra + rb;
       // ---- O^T += V^T P^T over the block's two 16-key halves
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -252,11 +285,66 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[c], o[d], 0, 0, 0);
         }
       }
+      if (kb + 1 < KB) {
+        if constexpr (BOUNDARY) apply_mask(sn, vmask, kb + 1);
+        rescale_if_needed(sn, m, l, o, c2, thr);
+        s = sn;
+      }
+    }
+  };
+
+  for (int j = beg; j < end; ++j) {
+    const int stage = (j - beg) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // The last tile re-copies itself into the idle buffer: harmless, and it
+    // keeps the copy steps free of branches.
+    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;
+    nbuf = lds + (stage ^ 1) * STAGE;
+    nk = kbase + (size_t)kv_copy * TILEB;
+    nv = vbase + (size_t)kv_copy * TILEB;
+    const int kv = kv_cur;
+    kv_cur = kv_nxt;
+    if (j + 2 < end) kv_nxt = kv_idx[j + 2];
+    const unsigned char* Ks = smem + stage * STAGE;
+    const unsigned char* Vs = Ks + TILEB;
+    if (!wave_active) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
+        tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
+      }
+    } else if ((j - beg) < nfull) {
+      tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
+    } else {
+      // Boundary tile: one validity bit per key this lane holds.  The lane's
+      // keys come in groups of 8 consecutive tile slots (g = 2 gg + hh); the
+      // KV tile's W extent is >= 8, so a group shares its (T, H) position and
+      // covers 8 consecutive W positions.  Bit 8 gg + t <-> slot 8 g + t.
+      const int k2 = (kv % p.nk2) << p.lk2;
+      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+      uint64_t vmask = 0;
+#pragma unroll 1
+      for (int gg = 0; gg < KVT / 16; ++gg) {
+        const int r0 = 8 * (2 * gg + hh);
+        const int lo = min(max(st2 - k2 - (r0 & km2), 0), 8);
+        const int hi = min(max(st2 + p.w2 - k2 - (r0 & km2), 0), 8);
+        const unsigned bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
+        const bool th = ((unsigned)(k0 + (r0 >> ksh) - st0) < (unsigned)p.w0) &
+                        ((unsigned)(k1 + ((r0 >> p.lk2) & km1) - st1) < (unsigned)p.w1);
+        vmask |= (uint64_t)(th ? bits : 0u) << (8 * gg);
+      }
+      tile_body(Ks, Vs, vmask, std::integral_constant<bool, true>{});
     }
   }
 
+  // the last step's copy must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
   // ---- epilogue: O / l in bf16, lse = m*scale + ln l
-  const float lt = xhalf_sum(l);
+  // padding-only waves store zeros (finite, meaningless rows)
+  const float lt = wave_active ? xhalf_sum(l) : 1.f;
   const float inv = 1.f / lt;
   __bf16* orow = static_cast<__bf16*>(p.ot) + (qtile * QT + row) * D;
 #pragma unroll
