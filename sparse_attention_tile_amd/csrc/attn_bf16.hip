@@ -42,6 +42,7 @@
 #include <type_traits>
 
 #include "attn_common.hpp"
+#include "attn_device.hpp"
 
 namespace na {
 namespace {
@@ -49,75 +50,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-
-// 16-byte chunk swizzle of a tile row with CPR chunks.
-template <int CPR>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (CPR >= 16) return row & 15;
-  else return (row >> 1) & (CPR - 1);
-}
 
 // Row of K fed to MFMA row `r` of a 32-key block: quads 1 and 2 of each
 // 16-row group swap places, so that accumulator i of lane half h holds key
 // 16*(i/8) + 8*h + i%8 of the block.
 __device__ __forceinline__ int kperm(int r) { return (((r >> 2) ^ (r >> 3)) & 1) ? (r ^ 12) : r; }
-
-__device__ __forceinline__ float xhalf_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xhalf_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Global -> LDS copy of one tile (rows of ROWB bytes), swizzled.  Each wave
-// moves 1 KiB per instruction: lane i fills LDS bytes [16 i, 16 i + 16) of
-// the wave's segment, so its global address picks the chunk that belongs
-// there.  Wave wv copies segments wv, wv + NW, ...; segment NW i + wv starts
-// 1024 NW i bytes after segment wv and the swizzle repeats within that
-// distance, so a lane's source offset is lane_off + 1024 NW i with lane_off
-// fixed for the whole kernel.
-template <int ROWB, int NW>
-__device__ __forceinline__ int dma_lane_offset(int wv, int lane) {
-  constexpr int CPR = ROWB / 16;
-  constexpr int ROUND = 1024 * NW;
-  static_assert(ROUND % ROWB == 0, "rows must divide the copy round");
-  static_assert((ROUND / ROWB) % 16 == 0, "swizzle period must divide the copy round");
-  const int byte = wv * 1024 + lane * 16;
-  const int row = byte / ROWB;
-  const int pc = (byte % ROWB) / 16;
-  return row * ROWB + ((pc ^ swz<CPR>(row)) * 16);
-}
-
-template <int TILEB, int NW>
-__device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds, int wv) {
-  constexpr int ROUND = 1024 * NW;
-  static_assert(TILEB % ROUND == 0, "tile must split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < TILEB / ROUND; ++i)
-    __builtin_amdgcn_global_load_lds(g + i * ROUND + lane_off,
-                                     (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0, 0);
-}
-
-// The rounds of a tile copy that belong to step kb of KB: the copy of the
-// next tile is spread over the current tile's key blocks, so the CU's vector
-// memory path sees a steady trickle instead of every wave's whole copy at
-// the barrier (which would stall all waves until the address queue drains).
-template <int TILEB, int NW, int KB>
-__device__ __forceinline__ void tile_to_lds_step(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds,
-                                                 int wv, int kb) {
-  constexpr int ROUND = 1024 * NW;
-  constexpr int ROUNDS = TILEB / ROUND;
-#pragma unroll
-  for (int i = 0; i < ROUNDS; ++i)
-    if ((i * KB) / ROUNDS == kb)
-      __builtin_amdgcn_global_load_lds(g + i * ROUND + lane_off,
-                                       (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0,
-                                       0);
-}
 
 // S^T block kb (32 keys x 32 queries) of the K tile at Ks.
 template <int D, int KROW>
@@ -131,14 +68,6 @@ __device__ __forceinline__ f32x16 qk_block(const unsigned char* Ks, int kb, int 
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[c], s, 0, 0, 0);
   }
   return s;
-}
-
-// Boundary tiles: accumulator i of block kb is key slot 32 kb + 16 (i/8) +
-// 8 hh + i%8, whose validity is bit 16 kb + i of the lane's mask.
-__device__ __forceinline__ void apply_mask(f32x16& s, uint64_t vmask, int kb) {
-  const unsigned mb = (unsigned)(vmask >> (16 * kb)) & 0xFFFFu;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] = ((mb >> i) & 1u) ? s[i] : -INFINITY;
 }
 
 // Lazy rescaling: move the reference max m only when the block max exceeds
@@ -293,52 +222,52 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     }
   };
 
-  for (int j = beg; j < end; ++j) {
+  // Barrier for tile j and bookkeeping of the next tile's copy; returns the
+  // LDS buffers holding tile j.
+  auto begin_tile = [&](int j, const unsigned char*& Ks, const unsigned char*& Vs) {
     const int stage = (j - beg) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    // The last tile re-copies itself into the idle buffer: harmless, and it
-    // keeps the copy steps free of branches.
-    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;
+    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
     nbuf = lds + (stage ^ 1) * STAGE;
     nk = kbase + (size_t)kv_copy * TILEB;
     nv = vbase + (size_t)kv_copy * TILEB;
     const int kv = kv_cur;
     kv_cur = kv_nxt;
     if (j + 2 < end) kv_nxt = kv_idx[j + 2];
-    const unsigned char* Ks = smem + stage * STAGE;
-    const unsigned char* Vs = Ks + TILEB;
-    if (!wave_active) {
+    Ks = smem + stage * STAGE;
+    Vs = Ks + TILEB;
+    return kv;
+  };
+
+  // Three homogeneous loops (padding-only waves copy; full tiles; boundary
+  // tiles), so the accumulators flow through simple loop phis.
+  const unsigned char* Ks;
+  const unsigned char* Vs;
+  if (!wave_active) {
+    for (int j = beg; j < end; ++j) {
+      begin_tile(j, Ks, Vs);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
         tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
       }
-    } else if ((j - beg) < nfull) {
+    }
+  } else {
+    for (int j = beg; j < beg + nfull; ++j) {
+      begin_tile(j, Ks, Vs);
       tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
-    } else {
-      // Boundary tile: one validity bit per key this lane holds.  The lane's
-      // keys come in groups of 8 consecutive tile slots (g = 2 gg + hh); the
-      // KV tile's W extent is >= 8, so a group shares its (T, H) position and
-      // covers 8 consecutive W positions.  Bit 8 gg + t <-> slot 8 g + t.
+    }
+    for (int j = beg + nfull; j < end; ++j) {
+      const int kv = begin_tile(j, Ks, Vs);
       const int k2 = (kv % p.nk2) << p.lk2;
       const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
       const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
-      uint64_t vmask = 0;
-#pragma unroll 1
-      for (int gg = 0; gg < KVT / 16; ++gg) {
-        const int r0 = 8 * (2 * gg + hh);
-        const int lo = min(max(st2 - k2 - (r0 & km2), 0), 8);
-        const int hi = min(max(st2 + p.w2 - k2 - (r0 & km2), 0), 8);
-        const unsigned bits = ((1u << hi) - 1u) & ~((1u << lo) - 1u);
-        const bool th = ((unsigned)(k0 + (r0 >> ksh) - st0) < (unsigned)p.w0) &
-                        ((unsigned)(k1 + ((r0 >> p.lk2) & km1) - st1) < (unsigned)p.w1);
-        vmask |= (uint64_t)(th ? bits : 0u) << (8 * gg);
-      }
+      const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1, st2, p.w0,
+                                                     p.w1, p.w2, p.lk2, km1, km2, ksh);
       tile_body(Ks, Vs, vmask, std::integral_constant<bool, true>{});
     }
   }
-
   // the last step's copy must land before the workgroup's LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 

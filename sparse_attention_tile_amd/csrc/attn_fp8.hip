@@ -1,13 +1,293 @@
-// fp8 (OCP e4m3fn) GNA attention: not built yet; the launcher reports the
-// dtype as unsupported so callers get NA_ERR_UNSUPPORTED.
+// fp8 (OCP e4m3fn) GNA attention forward on gfx950 matrix cores.
+//
+// Same method and workgroup structure as the bf16 kernel (GNA page, "GNA
+// Sparse Attention Mechanism: Vision-Transformer Compute Optimisation in
+// Practice", sections 1.1 and 2.1; the FP8 mode of section 2.1): q, k, v are
+// e4m3 with per-tensor dequantisation factors (q and k factors folded into
+// the softmax scale, the v factor into the epilogue); S and the softmax
+// statistics are fp32 (SLA page, "Sparse attention in video and image
+// generation: optimisation practice", section 3.1); the output is bf16.
+//
+// gfx950 mapping (differences from the bf16 kernel)
+// * Both products use v_mfma_scale_f32_32x32x64_f8f6f4 with unit block
+//   scales: S^T = K Q^T takes 64 head dims per instruction, O^T = V^T P^T 64
+//   keys per instruction.  The k index of this instruction is any assignment
+//   of (lane half, byte) to k that the A and B operands share, so each lane
+//   half simply takes 32 consecutive dims (QK) or two runs of 16 consecutive
+//   keys (PV).
+// * K rows are fed to the QK instruction so that accumulator i of lane half h
+//   is key 16 h + i of its 32-key block; two blocks then give a lane half the
+//   32 P bytes its PV B operand needs, straight from registers.
+// * P is stored as e4m3(64 p): the lazy-rescaling threshold is 2^2 here, so
+//   64 p <= 256 stays inside e4m3's range (448) while small weights keep
+//   precision.  l is computed by the matrix core from the same quantised P
+//   (an all-ones A operand), so O / l cancels the factor 64 exactly.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
 #include "attn_common.hpp"
+#include "attn_device.hpp"
 
 namespace na {
+namespace {
 
-bool attn_fp8_supported(int, int, int) { return false; }
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_attn_fp8(const AttnArgs&, hipStream_t) { return hipErrorInvalidValue; }
+constexpr float kPScaleLog2 = 6.f;   // P is stored as e4m3(2^6 p)
+constexpr float kLazyLog2 = 2.f;     // reference max moves when a block max exceeds it by 2^2
+
+// K row fed to MFMA row r of a 32-key block: r = 8 j + 4 h + t -> key
+// 16 h + 4 j + t, so accumulator i of lane half h holds key 16 h + i.
+__device__ __forceinline__ int kperm8(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
+
+__device__ __forceinline__ i32x8 lds_read32(const unsigned char* p0, const unsigned char* p1) {
+  const int4 a = *reinterpret_cast<const int4*>(p0);
+  const int4 b = *reinterpret_cast<const int4*>(p1);
+  return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+}
+
+__device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // formats: 0 = e4m3 for A and B; block scales 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int D, int NW, int KVT>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
+  constexpr int QT = NW * 32;            // queries per workgroup
+  constexpr int DS = D / 64;             // 64-dim k-steps of S^T
+  constexpr int DB = D / 32;             // 32-row blocks of O^T
+  constexpr int NSTEP = KVT / 64;        // 64-key steps per KV tile
+  constexpr int KROW = D;                // bytes per K row
+  constexpr int VROW = KVT;              // bytes per V^T row
+  constexpr int TILEB = KVT * D;         // bytes of one K (or V^T) tile
+  constexpr int STAGE = 2 * TILEB;
+  constexpr int KB = KVT / 32;           // copy steps per tile (one per 32-key block)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  lds_u8* lds = (lds_u8*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, hh = lane >> 5, lq = lane & 31;
+  const WorkItem wi = decode_work(p, blockIdx.x);
+  const size_t qtile = (size_t)wi.bh * p.nQ + wi.qrow;
+  const int row = wv * 32 + lq;
+
+  // ---- Q operand (B of S^T): query lq, dims 64 s + 32 hh .. + 31
+  i32x8 qr[DS];
+  {
+    const unsigned char* src = static_cast<const unsigned char*>(p.qt) + (qtile * QT + row) * D;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qr[s] = lds_read32(src + 64 * s + 32 * hh, src + 64 * s + 32 * hh + 16);
+  }
+  int st0, st1, st2;
+  bool wave_active;
+  {
+    const int px = row & ((1 << p.lq2) - 1);
+    const int py = (row >> p.lq2) & ((1 << p.lq1) - 1);
+    const int pt = row >> (p.lq1 + p.lq2);
+    const int gt = (wi.a0 << p.lq0) + pt, gy = (wi.a1 << p.lq1) + py, gx = (wi.a2 << p.lq2) + px;
+    st0 = dev_window_start(gt, p.L0, p.w0, p.s0);
+    st1 = dev_window_start(gy, p.L1, p.w1, p.s1);
+    st2 = dev_window_start(gx, p.L2, p.w2, p.s2);
+    wave_active = __builtin_amdgcn_ballot_w64(gt < p.L0 && gy < p.L1 && gx < p.L2) != 0;
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) o[d] = f32x16{};
+  f32x16 osum = f32x16{};                 // every row: sum of the stored P of this lane's query
+  float m = -INFINITY;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+
+  typedef const __attribute__((address_space(4))) int32_t cint;
+  const int qrow_u = __builtin_amdgcn_readfirstlane(wi.qrow);
+  const int beg = __builtin_amdgcn_readfirstlane(((cint*)p.qptr)[qrow_u]);
+  const int end = __builtin_amdgcn_readfirstlane(((cint*)p.qptr)[qrow_u + 1]);
+  const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u]);
+  cint* kv_idx = (cint*)p.kv_idx;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (size_t)wi.bh * p.nK * TILEB;
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * TILEB;
+  const float c2 = p.c2;
+  const int km2 = (1 << p.lk2) - 1, km1 = (1 << p.lk1) - 1, ksh = p.lk1 + p.lk2;
+  const int koff = dma_lane_offset<KROW, NW>(wv, lane);
+  const int voff = dma_lane_offset<VROW, NW>(wv, lane);
+  const float thr = c2 > 0.f ? kLazyLog2 / c2 : 3.0e38f;
+  const int krow0 = kperm8(lq);
+  const int kswz = swz<KROW / 16>(krow0);
+  const int vswz = swz<VROW / 16>(lq);
+
+  int kv_cur = kv_idx[beg];
+  int kv_nxt = beg + 1 < end ? kv_idx[beg + 1] : 0;
+  tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);
+  tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
+  const unsigned char* nk = kbase;
+  const unsigned char* nv = vbase;
+  lds_u8* nbuf = lds;
+
+  // S^T of 32-key block blk of the K tile at Ks
+  auto qk = [&](const unsigned char* Ks, int blk) {
+    f32x16 s = f32x16{};
+    const unsigned char* kr = Ks + (blk * 32 + krow0) * KROW;
+#pragma unroll
+    for (int t = 0; t < DS; ++t) {
+      const int c0 = 4 * t + 2 * hh;
+      const i32x8 a = lds_read32(kr + ((c0 ^ kswz) * 16), kr + (((c0 + 1) ^ kswz) * 16));
+      s = mfma8(a, qr[t], s);
+    }
+    return s;
+  };
+
+  auto tile_body = [&](const unsigned char* Ks, const unsigned char* Vs, uint64_t vmask, auto bnd) {
+    constexpr bool BOUNDARY = decltype(bnd)::value;
+#pragma unroll 1
+    for (int st = 0; st < NSTEP; ++st) {
+      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, 2 * st);
+      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, 2 * st);
+      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, 2 * st + 1);
+      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, 2 * st + 1);
+      f32x16 s0 = qk(Ks, 2 * st);
+      f32x16 s1 = qk(Ks, 2 * st + 1);
+      if constexpr (BOUNDARY) {
+        apply_mask(s0, vmask, 2 * st);
+        apply_mask(s1, vmask, 2 * st + 1);
+      }
+      float bm = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) bm = fmaxf(bm, fmaxf(s0[i], s1[i]));
+      bm = xhalf_max(bm);
+      if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {   // lazy rescaling, rare after the first steps
+        const float mn = fmaxf(m, bm);
+        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        osum *= alpha;
+        m = mn;
+      }
+      // P bytes: byte j < 16 is key 16 hh + j of block 2 st, byte 16 + j key 16 hh + j of block 2 st + 1
+      const float nref = (m == -INFINITY ? 0.f : -m * c2) + kPScaleLog2;
+      i32x8 pb;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q], c2, nref)),
+                                                 __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 1], c2, nref)), 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q + 2], c2, nref)),
+                                             __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 3], c2, nref)), w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q], c2, nref)),
+                                                 __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 1], c2, nref)), 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q + 2], c2, nref)),
+                                             __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 3], c2, nref)), w1, true);
+        pb[q] = w0;
+        pb[4 + q] = w1;
+      }
+      // O^T += V^T P^T (64 keys), and the row sums through an all-ones A
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const unsigned char* vr = Vs + (d * 32 + lq) * VROW;
+        const int c0 = 4 * st + hh, c1 = 4 * st + 2 + hh;
+        const i32x8 a = lds_read32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
+        o[d] = mfma8(a, pb, o[d]);
+      }
+      osum = mfma8(ones, pb, osum);
+    }
+  };
+
+  // Barrier for tile j and bookkeeping of the next tile's copy; returns the
+  // LDS buffers holding tile j.
+  auto begin_tile = [&](int j, const unsigned char*& Ks, const unsigned char*& Vs) {
+    const int stage = (j - beg) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
+    nbuf = lds + (stage ^ 1) * STAGE;
+    nk = kbase + (size_t)kv_copy * TILEB;
+    nv = vbase + (size_t)kv_copy * TILEB;
+    const int kv = kv_cur;
+    kv_cur = kv_nxt;
+    if (j + 2 < end) kv_nxt = kv_idx[j + 2];
+    Ks = smem + stage * STAGE;
+    Vs = Ks + TILEB;
+    return kv;
+  };
+
+  // Three homogeneous loops (padding-only waves copy; full tiles; boundary
+  // tiles), so the accumulators flow through simple loop phis.
+  const unsigned char* Ks;
+  const unsigned char* Vs;
+  if (!wave_active) {
+    for (int j = beg; j < end; ++j) {
+      begin_tile(j, Ks, Vs);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
+        tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
+      }
+    }
+  } else {
+    for (int j = beg; j < beg + nfull; ++j) {
+      begin_tile(j, Ks, Vs);
+      tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
+    }
+    for (int j = beg + nfull; j < end; ++j) {
+      const int kv = begin_tile(j, Ks, Vs);
+      const int k2 = (kv % p.nk2) << p.lk2;
+      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+      const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 32 * (gg >> 1) + 16 * hh + 8 * (gg & 1); }, k0, k1, k2, st0, st1, st2, p.w0,
+                                                     p.w1, p.w2, p.lk2, km1, km2, ksh);
+      tile_body(Ks, Vs, vmask, std::integral_constant<bool, true>{});
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: out = v_scale * O / l (the factor 64 of P cancels), bf16
+  const float lt = wave_active ? osum[0] : 1.f;
+  const float mult = p.v_scale / lt;
+  __bf16* orow = static_cast<__bf16*>(p.ot) + (qtile * QT + row) * D;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 v;
+      v[0] = (__bf16)(o[d][4 * g + 0] * mult);
+      v[1] = (__bf16)(o[d][4 * g + 1] * mult);
+      v[2] = (__bf16)(o[d][4 * g + 2] * mult);
+      v[3] = (__bf16)(o[d][4 * g + 3] * mult);
+      *reinterpret_cast<bf16x4*>(orow + d * 32 + 8 * g + 4 * hh) = v;
+    }
+  }
+  if (p.lse_t && hh == 0)
+    p.lse_t[qtile * QT + row] =
+        m == -INFINITY ? 0.f : m * p.scale + logf(lt) - kPScaleLog2 * 0.69314718055994531f;
+}
+
+template <int NW, int KVT>
+hipError_t launch_cfg(const KParams& p, hipStream_t st) {
+  attn_fp8_kernel<128, NW, KVT><<<p.num_wg, NW * 64, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_fp8_supported(int head_dim, int q_tokens, int kv_tokens) {
+  return head_dim == 128 && (q_tokens == 128 || q_tokens == 256) && (kv_tokens == 64 || kv_tokens == 128);
+}
+
+hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t st) {
+  const KParams p = make_kparams(a);
+  const int qtok = a.tq[0] * a.tq[1] * a.tq[2];
+  const int ktok = a.tkv[0] * a.tkv[1] * a.tkv[2];
+  if (!attn_fp8_supported(a.head_dim, qtok, ktok) || !attn_bf16_tile_ok(a.tkv)) return hipErrorInvalidValue;
+  const int key = (qtok == 256 ? 2 : 0) | (ktok == 128 ? 1 : 0);
+  switch (key) {
+    case 0: return launch_cfg<4, 64>(p, st);
+    case 1: return launch_cfg<4, 128>(p, st);
+    case 2: return launch_cfg<8, 64>(p, st);
+    default: return launch_cfg<8, 128>(p, st);
+  }
+}
 
 }  // namespace na

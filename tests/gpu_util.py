@@ -10,9 +10,12 @@ import torch
 import oracle
 from synth import make_qkv, to_f64
 
-# max-abs tolerances on N(0,1) inputs (out: from the workload spec; lse: ours,
-# from the fp32 softmax statistics and v_exp_f32 rounding)
-TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-3), "fp8": (6e-2, 1e-2)}
+# max-abs tolerances on N(0,1) inputs.  out: the workload specification's
+# bounds.  lse: fp32 / bf16 from the fp32 softmax statistics and v_exp_f32
+# rounding; fp8 from the e4m3 quantisation of P: l sums weights that each carry
+# a relative rounding error of at most 2^-4 (3 mantissa bits), so
+# |d lse| <= ln(1 + 2^-4) = 0.0606.
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-3), "fp8": (6e-2, 6.1e-2)}
 
 
 def say(*a):

@@ -28,7 +28,7 @@ def test_small_workloads_all_queries(na, name):
 
 
 @pytest.mark.parametrize("name,heads", [("video_block", (0, 23)), ("video_sliding", (5,)),
-                                        ("img256_block", (0, 17))])
+                                        ("img256_block", (0, 17)), ("img256_block_fp8", (3, 20))])
 def test_full_size_sampled(na, name, heads):
     wl = WORKLOADS[name]
     qc, kc, vc, sc, q, k, v = inputs(wl)
@@ -82,3 +82,21 @@ def test_f32_head_dims(na, D):
     eo, el = compare(wl, qc, kc, vc, sc, out, lse)
     say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
     assert eo <= TOL["f32"][0] and el <= TOL["f32"][1]
+
+
+FP8_VARIANTS = [("4,8,8", "2,8,8"), ("2,8,8", "1,8,8"), ("4,8,8", "1,8,8"), ("2,8,8", "2,8,8")]
+
+
+@pytest.mark.parametrize("tq,tk", FP8_VARIANTS)
+def test_fp8_kernel_variants_ragged_grid(na, monkeypatch, tq, tk):
+    wl = WORKLOADS["img256_block_fp8"].with_(name="ragged8", batch=2, heads=2, grid=(5, 19, 27),
+                                             window=(3, 7, 9), stride=(1, 2, 3), seed=778)
+    monkeypatch.setenv("NA_TILE_Q", tq)
+    monkeypatch.setenv("NA_TILE_KV", tk)
+    say(f"[parity] fp8 variant tq={tq} tk={tk} grid={wl.grid}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse, f = run_hip(na, wl, q, k, v, sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    to, tl = TOL["fp8"]
+    assert eo <= to and el <= tl

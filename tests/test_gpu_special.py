@@ -163,3 +163,17 @@ def test_no_lse_and_empty_batch(na):
     e = torch.empty((0, 1, 64, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
     o, l = na.forward(e, e, e, (1, 17, 17), (1, 1, 1))
     assert o.shape == e.shape and l.shape == e.shape[:-1]
+
+
+def test_fp8_window_one_returns_scaled_v_exactly(na):
+    # window 1: P = e4m3(64) exactly, l = 64, out = bf16(v8 * v_scale)
+    wl = WORKLOADS["img256_block_fp8"].with_(grid=(2, 13, 24), window=(1, 1, 1), stride=(1, 1, 1), heads=2, seed=99)
+    say("[special] fp8 window 1")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, qkv_scale=sc)
+    out, lse = f()
+    torch.cuda.synchronize()
+    ref = (vc.float() * sc[2]).to(torch.bfloat16)
+    assert torch.equal(out.cpu(), ref)
+    lref = wl.scale * sc[0] * sc[1] * (qc.double() * kc.double()).sum(-1)
+    assert float((lse.cpu().double() - lref).abs().max()) <= TOL["fp8"][1]
