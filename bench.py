@@ -2,17 +2,20 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video_block]
 
-One step = one complete forward (na_forward: permute q, k, v to tile order,
-the fused attention kernel, permute out and lse back) over one batch of
-seeded synthetic input that is already resident in HBM.  The default
+One step = one complete forward (na_forward) over one batch of seeded
+synthetic input that is already resident in HBM.  For bf16 that is one
+kernel reading q, k, v in grid order and writing out and lse in grid order;
+for fp8 / fp32 it is permute q, k, v to tile order, the tiled attention
+kernel, permute out and lse back.  The default
 workload is the 91 %-sparse 3-D video configuration (batch 1, 24 heads,
 30x48x80 tokens, head_dim 128, window 18x24x24, stride 16x8x8, bf16).
 
 Prints ONE JSON line: effective TFLOP/s (only unmasked QK^T + PV FLOPs,
 4 * b * h * N * prod(window) * D per call) of the whole forward, ms per step,
-the per-stage times measured with HIP events on the launch stream, the
-roofline of the attention kernel, the dense full-window speed-up reference
-and the CPU oracle timed on a bounded sample.
+the roofline of the attention kernel the step runs, the stage times of the
+permute -> tiled kernel -> unpermute form (HIP events on the launch stream)
+for comparison, the dense full-window speed-up reference and the CPU oracle
+timed on a bounded sample.
 """
 
 from __future__ import annotations
@@ -55,16 +58,16 @@ def time_steps(torch, fn, steps, warmup):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "attn_common.hpp"):
+    for f in ("attn_bf16.hip", "attn_common.hpp", "attn_device.hpp"):
         with open(os.path.join(ROOT, "sparse_attention_tile_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, src_hash):
+def measured_traffic(workload, src_hash, kform):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "attn_bf16_video_block_traffic.json")
+    summary, if it was taken on the current kernel source and form; else None."""
+    path = os.path.join(ROOT, "profiles", f"attn_bf16_{kform.lower()}_{workload}_traffic.json")
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -161,20 +164,24 @@ def main():
     stream = torch.cuda.current_stream().cuda_stream
     tq, tk = fwd.tile_q, fwd.tile_kv
     eb = q.element_size()
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    mode = fwd.mode
+    st_steps = max(5, args.steps)
     qt = na.permute(q, tq)
     kt = na.permute(k, tk)
     vt = na.permute(v, tk, transpose=(dcode != na.NA_F32))
     out_dtype = torch.float32 if dcode == na.NA_F32 else torch.bfloat16
     ot = torch.empty(qt.shape, dtype=out_dtype, device="cuda")
     lt = torch.empty(qt.shape[:-1], dtype=torch.float32, device="cuda")
-    B, H, D = wl.batch, wl.heads, wl.head_dim
 
-    def attn():
+    def attn_tiled():
         na.na_attend_tiled(qt.data_ptr(), kt.data_ptr(), vt.data_ptr(), ot.data_ptr(), lt.data_ptr(), B, H, D,
                            wl.grid, wl.window, wl.stride, tq, tk, wl.scale, dcode, sc if fp8 else None, stream)
 
-    def perm_qkv():
+    def perm_q():
         na.na_permute(q.data_ptr(), qt.data_ptr(), B, H, D, wl.grid, tq, eb, 0, stream)
+
+    def perm_kv():
         na.na_permute(k.data_ptr(), kt.data_ptr(), B, H, D, wl.grid, tk, eb, 0, stream)
         na.na_permute(v.data_ptr(), vt.data_ptr(), B, H, D, wl.grid, tk, eb, int(dcode != na.NA_F32), stream)
 
@@ -182,23 +189,39 @@ def main():
         na.na_unpermute(ot.data_ptr(), fwd.out.data_ptr(), B, H, D, wl.grid, tq, ot.element_size(), stream)
         na.na_unpermute_lse(lt.data_ptr(), fwd.lse.data_ptr(), B, H, wl.grid, tq, stream)
 
-    st_steps = max(5, args.steps)
-    a_per, a_tot = time_steps(torch, attn, st_steps, 2)
-    attn_ms = a_tot / st_steps
-    p_per, p_tot = time_steps(torch, perm_qkv, st_steps, 2)
-    perm_ms = p_tot / st_steps
-    u_per, u_tot = time_steps(torch, unperm, st_steps, 2)
-    unperm_ms = u_tot / st_steps
-    perm_bytes = q.numel() * eb * 3 + (qt.numel() + kt.numel() + vt.numel()) * eb
-    unperm_bytes = ot.numel() * ot.element_size() + fwd.out.numel() * fwd.out.element_size() + \
-        lt.numel() * 4 + fwd.lse.numel() * 4
+    def attn_qo():
+        na.na_attend_kv_tiled(q.data_ptr(), kt.data_ptr(), vt.data_ptr(), fwd.out.data_ptr(), fwd.lse.data_ptr(),
+                              B, H, D, wl.grid, wl.window, wl.stride, tk, wl.scale, dcode, stream)
+
+    def stage_ms(fn):
+        _, tot = time_steps(torch, fn, st_steps, 2)
+        return tot / st_steps
+
+    perm_q_ms, perm_kv_ms = stage_ms(perm_q), stage_ms(perm_kv)
+    attn_tiled_ms, unperm_ms = stage_ms(attn_tiled), stage_ms(unperm)
+    stages = {"tiled_form": {"permute_q": perm_q_ms, "permute_kv": perm_kv_ms, "attention_tiled": attn_tiled_ms,
+                             "unpermute_out_lse": unperm_ms,
+                             "total": perm_q_ms + perm_kv_ms + attn_tiled_ms + unperm_ms}}
+    if mode == 1:
+        attn_qo_ms = stage_ms(attn_qo)
+        stages["kv_copy_form"] = {"permute_kv": perm_kv_ms, "attention_q_out_grid_order": attn_qo_ms,
+                                  "total": perm_kv_ms + attn_qo_ms}
+        nw = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=False)
+        stages["no_workspace_form"] = {"total": stage_ms(nw)}
+        del nw
+    kernel_ms = {0: attn_tiled_ms, 1: stages.get("kv_copy_form", {}).get("attention_q_out_grid_order"),
+                 2: ms}[mode]
+    perm_bytes = (q.numel() * 2 + kt.numel() + vt.numel()) * eb
+    del qt, ot, lt
 
     _, _, _, tstats = na.na_build_tile_map(wl.grid, wl.window, wl.stride, tq, tk)
     computed = 4.0 * B * H * tstats["computed_slots"] * D
     peak = PEAK_TFLOPS[wl.dtype]
-    achieved = eff / (attn_ms * 1e-3) / 1e12
+    achieved = eff / (kernel_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
-    traffic = measured_traffic(wl.name, src_hash)
+    kname = {na.NA_BF16: "attn_bf16_kernel", na.NA_FP8_E4M3: "attn_fp8_kernel", na.NA_F32: "attn_f32_kernel"}[dcode]
+    kform = {0: "IO_TILE", 1: "IO_QO", 2: "IO_GRID"}[mode]
+    traffic = measured_traffic(wl.name, src_hash, kform)
 
     result = {
         "metric": "effective TFLOP/s (unmasked FLOPs) of one GNA forward, 1 MI355X",
@@ -224,11 +247,14 @@ def main():
         "pct_of_peak": 100.0 * (eff / (ms * 1e-3) / 1e12) / peak,
         "step_ms_median": med,
         "step_ms_std_over_median": std / med,
-        "stages_ms": {"permute_qkv": perm_ms, "attention": attn_ms, "unpermute_out_lse": unperm_ms},
-        "permute_GBps": perm_bytes / (perm_ms * 1e-3) / 1e9,
-        "unpermute_GBps": unperm_bytes / (unperm_ms * 1e-3) / 1e9,
+        "form": {0: "permute q, k, v -> tiled kernel -> unpermute out, lse",
+                 1: "permute k, v -> kernel reading q / writing out, lse in grid order",
+                 2: "one kernel, everything in grid order"}[mode],
+        "stages_ms": stages,
+        "permute_GBps": perm_bytes / ((perm_q_ms + perm_kv_ms) * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "attn_bf16_kernel" if dcode == na.NA_BF16 else "attention",
+            "kernel": f"{kname}<{kform}>",
+            "kernel_ms": kernel_ms,
             "bound": "mfma",
             "achieved": achieved,
             "peak": peak,

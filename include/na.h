@@ -125,14 +125,26 @@ na_status na_build_tile_map(const int grid[3], const int window[3],
                             int64_t kv_capacity, int64_t* nnz_out,
                             na_tilemap_stats* stats);
 
-/* Bytes of device workspace na_forward needs for this problem (the
- * tile-ordered copies of q, k, v, out and lse).  It grows linearly with the
- * token count: no N x N buffer exists (tutorial, section 3.3).  Returns 0 if
+/* Bytes of device workspace na_forward needs for this problem: the
+ * tile-ordered copies it makes (form 1 of na_forward_mode: k and v; form 0:
+ * q, k, v, out and lse).  It grows linearly with the token count: no N x N
+ * buffer exists (tutorial, section 3.3).  Returns 0 if
  * the arguments are invalid or unsupported (na_last_error() says why) and
  * for an empty problem (then na_last_error() is ""). */
 size_t na_workspace_bytes(int batch, int heads, int head_dim,
                           const int grid[3], const int window[3],
                           const int stride[3], na_dtype dtype);
+
+/* The form na_forward takes for this dtype and head_dim:
+ *   0  permute q, k, v to tile order, tiled kernel, unpermute out and lse;
+ *   1  permute k, v only; the kernel reads q and writes out and lse in grid
+ *      order (bf16, head_dim 64 / 128, with a workspace);
+ *   2  no permutation and no workspace: the kernel also gathers the k / v
+ *      tiles from grid order (bf16, head_dim 64 / 128, workspace NULL).
+ * with_workspace says whether the call would pass a workspace.  The
+ * environment variable NA_NO_FUSED=1, read at each call, forces form 0 (a
+ * test hook).  Never fails. */
+int na_forward_mode(na_dtype dtype, int head_dim, int with_workspace);
 
 /* Message of the last failing call on this thread ("" if none).  Valid
  * until the next call on the same thread. */
@@ -146,9 +158,21 @@ void na_release_cache(void);
 /* Device entry points (enqueue on `stream`).                             */
 /* ---------------------------------------------------------------------- */
 
-/* One GNA forward pass (GNA page, sections 1.1 and 2.1-2.2):
- *   permute q, k, v to tile order (zero padding), run the fused tiled
+/* One GNA forward pass (GNA page, sections 1.1 and 2.1-2.2).
+ *   bf16 (head_dim 64/128) with a workspace: permute k and v to tile order;
+ *   one kernel reads the q rows and writes out and lse in grid order.
+ *   bf16 (head_dim 64/128) with workspace == NULL: no permutation at all --
+ *   the kernel also gathers the k / v tiles from grid order (the permutation
+ *   the page plans to fuse away, section 2.2, does not exist).  Slower than
+ *   the form above on the video workload (the token-by-token gather), but
+ *   needs no memory beyond the outputs.
+ *   fp32 and fp8: permute q, k, v to tile order (zero padding), run the tiled
  *   attention kernel, permute out and lse back to grid order.
+ * na_forward_mode() tells which form a call takes.  When q is read in grid
+ * order, the padding slots of ragged Q tiles read real tokens of the grid
+ * (results discarded); when k / v are gathered, padding slots of ragged KV
+ * tiles read real tokens (masked, multiplied by zero).  So q, k, v must hold
+ * finite values everywhere, not only inside the windows.
  *
  * q, k, v  device, [batch, T, H, W, heads, head_dim], dtype `dtype`.
  * out      device, same shape; fp32 for NA_F32, bf16 for NA_BF16 and
@@ -159,7 +183,8 @@ void na_release_cache(void);
  *          finite and >= 0 (a negative factor belongs in q).
  * qkv_scale host, 3 floats: dequantisation multipliers of q, k, v for
  *          NA_FP8_E4M3 (NULL means 1, 1, 1); ignored for other dtypes.
- * workspace device, caller-owned, >= na_workspace_bytes(...) bytes.
+ * workspace device, caller-owned, >= na_workspace_bytes(...) bytes; may be
+ *          NULL for bf16 with head_dim 64 / 128 (workspace_bytes ignored).
  * head_dim must be 32 (NA_F32), 64 or 128 (NA_BF16, NA_FP8_E4M3).
  *
  * Softmax statistics and accumulation are fp32 in every mode (SLA page,
@@ -218,6 +243,22 @@ na_status na_attend_tiled(const void* qt, const void* kt, const void* vt,
                           const int stride[3], const int tile_q[3],
                           const int tile_kv[3], float scale, na_dtype dtype,
                           const float* qkv_scale, void* stream);
+
+/* The attention kernel of na_forward's form 1 alone (GNA page, sections 1.1
+ * and 2.1-2.2): q, out and lse in grid order, k and v already in tile order
+ * (as na_permute writes them: kt plain, vt transposed, both with tile_kv
+ * tiles).  bf16 with head_dim 64 or 128 only (else NA_ERR_UNSUPPORTED).
+ *
+ * q, out  device, [batch, T, H, W, heads, head_dim] bf16.
+ * lse     device, [batch, T, H, W, heads] fp32, or NULL.
+ * tile_kv must be what na_choose_tiles returns for the problem.
+ * Other arguments as for na_forward. */
+na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt,
+                             void* out, float* lse, int batch, int heads,
+                             int head_dim, const int grid[3],
+                             const int window[3], const int stride[3],
+                             const int tile_kv[3], float scale, na_dtype dtype,
+                             void* stream);
 
 #ifdef __cplusplus
 }

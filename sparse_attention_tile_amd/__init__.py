@@ -22,8 +22,9 @@ NA_OK, NA_ERR_INVALID_ARG, NA_ERR_UNSUPPORTED, NA_ERR_WORKSPACE, NA_ERR_HIP = 0,
 NA_F32, NA_BF16, NA_FP8_E4M3 = 0, 1, 2
 
 SYMBOLS = (
-    "na_choose_tiles", "na_build_tile_map", "na_workspace_bytes", "na_last_error", "na_release_cache",
-    "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
+    "na_choose_tiles", "na_build_tile_map", "na_workspace_bytes", "na_forward_mode", "na_last_error",
+    "na_release_cache", "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
+    "na_attend_kv_tiled",
 )
 
 
@@ -59,6 +60,7 @@ def load():
         "na_build_tile_map": ([I3, I3, I3, I3, I3, _p, _p, _p, ctypes.c_int64,
                                ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(TileMapStats)], _i),
         "na_workspace_bytes": ([_i, _i, _i, I3, I3, I3, _i], ctypes.c_size_t),
+        "na_forward_mode": ([_i, _i], _i),
         "na_last_error": ([], ctypes.c_char_p),
         "na_release_cache": ([], None),
         "na_forward": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _fp, _p,
@@ -68,6 +70,7 @@ def load():
         "na_unpermute_lse": ([_p, _p, _i, _i, I3, I3, _p], _i),
         "na_attend_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, I3, ctypes.c_float, _i, _fp,
                              _p], _i),
+        "na_attend_kv_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, ctypes.c_float, _i, _p], _i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -124,6 +127,12 @@ def na_build_tile_map(grid, window, stride, tile_q, tile_kv):
     return qptr, kv[: nnz.value], nf, stats
 
 
+def na_forward_mode(dtype, head_dim, with_workspace=True) -> int:
+    """Form of na_forward: 0 permute q, k, v (+ unpermute), 1 permute k, v only,
+    2 no permutation (bf16 without a workspace)."""
+    return int(load().na_forward_mode(dtype, head_dim, int(bool(with_workspace))))
+
+
 def na_workspace_bytes(batch, heads, head_dim, grid, window, stride, dtype) -> int:
     n = load().na_workspace_bytes(batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride), dtype)
     if n == 0 and na_last_error():
@@ -155,6 +164,12 @@ def na_attend_tiled(qt, kt, vt, ot, lse_t, batch, heads, head_dim, grid, window,
     qs = (ctypes.c_float * 3)(*qkv_scale) if qkv_scale is not None else None
     _check(load().na_attend_tiled(qt, kt, vt, ot, lse_t, batch, heads, head_dim, _i3(grid), _i3(window),
                                   _i3(stride), _i3(tile_q), _i3(tile_kv), scale, dtype, qs, stream))
+
+
+def na_attend_kv_tiled(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, tile_kv, scale, dtype,
+                       stream):
+    _check(load().na_attend_kv_tiled(q, kt, vt, out, lse, batch, heads, head_dim, _i3(grid), _i3(window),
+                                     _i3(stride), _i3(tile_kv), scale, dtype, stream))
 
 
 # ---------------------------------------------------------------------------
@@ -199,7 +214,7 @@ class Forward:
     """A prepared GNA forward call: validates once, owns the workspace and the
     outputs, and enqueues na_forward on each call (no allocation per call)."""
 
-    def __init__(self, q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=True):
+    def __init__(self, q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=True, workspace=True):
         torch = _torch()
         load()
         for t in (q, k, v):
@@ -218,9 +233,13 @@ class Forward:
         out_dtype = torch.float32 if self.dtype == NA_F32 else torch.bfloat16
         self.out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
         self.lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if return_lse else None
-        self.ws_bytes = na_workspace_bytes(self.batch, self.heads, self.head_dim, self.grid, self.window,
-                                           self.stride, self.dtype)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=q.device)
+        if workspace:
+            self.ws_bytes = na_workspace_bytes(self.batch, self.heads, self.head_dim, self.grid, self.window,
+                                               self.stride, self.dtype)
+            self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=q.device)
+        else:   # permutation-free form (bf16, head_dim 64 / 128); else na_forward fails
+            self.ws_bytes, self.workspace = 0, None
+        self.mode = na_forward_mode(self.dtype, self.head_dim, workspace)
         self.tile_q, self.tile_kv = na_choose_tiles(self.grid, self.window, self.stride, self.head_dim, self.dtype)
         self.q, self.k, self.v = q, k, v
 
@@ -228,16 +247,17 @@ class Forward:
         na_forward(self.q.data_ptr(), self.k.data_ptr(), self.v.data_ptr(), self.out.data_ptr(),
                    self.lse.data_ptr() if self.lse is not None else None, self.batch, self.heads, self.head_dim,
                    self.grid, self.window, self.stride, self.scale, self.dtype, self.qkv_scale,
-                   self.workspace.data_ptr(), self.ws_bytes, _stream_ptr(stream))
+                   self.workspace.data_ptr() if self.workspace is not None else None, self.ws_bytes,
+                   _stream_ptr(stream))
         return self.out, self.lse
 
 
-def forward(q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=True, stream=None):
+def forward(q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=True, stream=None, workspace=True):
     """GNA forward of device tensors q, k, v ([B, *grid, heads, D]).
 
     Returns (out, lse): out has q's shape (bf16 for fp8 input), lse is
     [B, *grid, heads] fp32 (None if return_lse is False)."""
-    f = Forward(q, k, v, window, stride, scale, qkv_scale, return_lse)
+    f = Forward(q, k, v, window, stride, scale, qkv_scale, return_lse, workspace)
     return f(stream)
 
 

@@ -91,15 +91,65 @@ __device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, flo
   }
 }
 
-template <int D, int NW, int KVT>
+// Tensor layouts (IO mode, a template parameter of the kernel):
+//  IO_TILE: q, k, v, out, lse in tile order (na_permute output; V transposed
+//           per tile).
+//  IO_QO:   q, out, lse are the caller's grid-order tensors (each query row is
+//           read and written in place), k and v in tile order.
+//  IO_GRID: all five in grid order; K / V tiles are gathered token by token
+//           (the LDS-DMA takes one source address per lane), V stays [key][d]
+//           in LDS and its PV operand is read with the transposing LDS load --
+//           no permutation pass and no workspace at all.
+// Copy step kb of a tile whose per-round source offsets (from base) are off[].
+template <int TILEB, int NW, int KB, int ROUNDS>
+__device__ __forceinline__ void tile_to_lds_step_off(const unsigned char* __restrict__ base,
+                                                     const int64_t (&off)[ROUNDS], lds_u8* lds, int wv, int kb) {
+  constexpr int ROUND = 1024 * NW;
+  static_assert(TILEB / ROUND == ROUNDS, "one offset per copy round");
+#pragma unroll
+  for (int i = 0; i < ROUNDS; ++i)
+    if ((i * KB) / ROUNDS == kb)
+      __builtin_amdgcn_global_load_lds(base + off[i],
+                                       (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0,
+                                       0);
+}
+
+// A operand of O^T = V^T P^T (32 head dims x 16 keys: keys key0 .. key0+15 of
+// the tile, dims 32 db .. 32 db + 31) from a V tile stored [key][d] (rows of
+// 2 D bytes, K's chunk swizzle), with two transposing LDS reads.  Within each
+// group of 16 lanes the read hands lane 4 a + b element b of the 8-byte chunks
+// addressed by lanes a, a + 4, a + 8, a + 12; so lane i of group g addresses
+// key key0 + 8 (g / 2) + 4 r + i / 4 at dims 32 db + 16 (g % 2) + 4 (i % 4),
+// and lane l then holds dim 32 db + l % 32 for keys key0 + 8 (l / 32) + 0..7,
+// the order of the P operand.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand_tr(const unsigned char* Vs, int key0, int db, int lane) {
+  constexpr int ROWB = D * 2;
+  const int g = lane >> 4, i = lane & 15;
+  const int dcol = 32 * db + 16 * (g & 1) + 4 * (i & 3);          // first of 4 dims
+  const int chunk = (dcol * 2) >> 4, sub = (dcol * 2) & 15;
+  bf16x4 h[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = key0 + 8 * (g >> 1) + 4 * r + (i >> 2);
+    const unsigned char* a = Vs + key * ROWB + ((chunk ^ swz<ROWB / 16>(key)) * 16) + sub;
+    h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a);
+  }
+  return bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+}
+
+template <int D, int NW, int KVT, int IO>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
+  constexpr bool GQ = IO != IO_TILE;     // q, out, lse in grid order
+  constexpr bool GKV = IO == IO_GRID;    // k, v in grid order
   constexpr int QT = NW * 32;            // queries per workgroup
   constexpr int DC = D / 16;             // k-steps of S^T
   constexpr int DB = D / 32;             // 32-row blocks of O^T
   constexpr int KB = KVT / 32;           // 32-key blocks per KV tile
   constexpr int KROW = D * 2;            // bytes per K row
-  constexpr int VROW = KVT * 2;          // bytes per V^T row
-  constexpr int TILEB = KVT * D * 2;     // bytes of one K (or V^T) tile
+  constexpr int VROW = GKV ? D * 2 : KVT * 2;    // bytes per V row (GKV) or V^T row
+  constexpr int TILEB = KVT * D * 2;     // bytes of one K (or V) tile
+  constexpr int ROUNDS = TILEB / (1024 * NW);    // copy rounds per tile
   constexpr int STAGE = 2 * TILEB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   lds_u8* lds = (lds_u8*)smem;
@@ -110,18 +160,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const size_t qtile = (size_t)wi.bh * p.nQ + wi.qrow;
   const int row = wv * 32 + lq;          // this lane's query inside the Q tile
 
-  // ---- Q operand (B of S^T = K Q^T): query = lane % 32, 8 dims per lane
-  bf16x8 qr[DC];
-  {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.qt) + (qtile * QT + row) * D);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) qr[c] = src[2 * c + hh];
-  }
-  // this query's window on each axis (for boundary tiles), and whether the
-  // wave holds any real query: a wave whose 32 slots are all padding (ragged
-  // grid edge) skips the arithmetic and only helps with the tile copies
+  // this query's grid position and window on each axis (for boundary tiles),
+  // and whether the wave holds any real query: a wave whose 32 slots are all
+  // padding (ragged grid edge) skips the arithmetic and only helps with the
+  // tile copies
   int st0, st1, st2;
-  bool wave_active;
+  bool wave_active, q_valid;
+  int q_tok;                             // grid token of the query (clamped inside the grid)
   {
     const int px = row & ((1 << p.lq2) - 1);
     const int py = (row >> p.lq2) & ((1 << p.lq1) - 1);
@@ -130,7 +175,24 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     st0 = dev_window_start(gt, p.L0, p.w0, p.s0);
     st1 = dev_window_start(gy, p.L1, p.w1, p.s1);
     st2 = dev_window_start(gx, p.L2, p.w2, p.s2);
-    wave_active = __builtin_amdgcn_ballot_w64(gt < p.L0 && gy < p.L1 && gx < p.L2) != 0;
+    q_valid = gt < p.L0 && gy < p.L1 && gx < p.L2;
+    wave_active = __builtin_amdgcn_ballot_w64(q_valid) != 0;
+    q_tok = (min(gt, p.L0 - 1) * p.L1 + min(gy, p.L1 - 1)) * p.L2 + min(gx, p.L2 - 1);
+  }
+  // grid-order element offset of token 0 of this (batch, head), and the
+  // element stride between tokens
+  const int bb = wi.bh / p.heads, hd = wi.bh % p.heads;
+  const size_t grid_base = ((size_t)bb * p.L0 * p.L1 * p.L2 * p.heads + hd) * D;
+  const size_t tok_stride = (size_t)p.heads * D;
+
+  // ---- Q operand (B of S^T = K Q^T): query = lane % 32, 8 dims per lane
+  bf16x8 qr[DC];
+  {
+    const __bf16* qrow = static_cast<const __bf16*>(p.qt) +
+                         (GQ ? grid_base + (size_t)q_tok * tok_stride : (qtile * QT + row) * D);
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(qrow);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) qr[c] = src[2 * c + hh];
   }
 
   f32x16 o[DB];
@@ -148,8 +210,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const int beg = __builtin_amdgcn_readfirstlane(qptr[qrow_u]);
   const int end = __builtin_amdgcn_readfirstlane(qptr[qrow_u + 1]);
   const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u]);
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (size_t)wi.bh * p.nK * TILEB;
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * TILEB;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
   const float c2 = p.c2;
   const int km2 = (1 << p.lk2) - 1, km1 = (1 << p.lk1) - 1, ksh = p.lk1 + p.lk2;
   static_assert(KVT / 16 <= 8, "validity mask holds 64 bits");
@@ -162,13 +224,46 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const int kswz = swz<KROW / 16>(krow0);
   const int vswz = swz<VROW / 16>(lq);
 
+  // GKV: the token each lane copies in copy round i sits at in-tile slot
+  // dslot[i]; its byte offset from the (batch, head) base depends on the tile
+  // and is computed per tile in grid_offsets (padding slots are clamped to a
+  // real token: finite data that the mask multiplies by zero).
+  int dslot[ROUNDS > 0 ? ROUNDS : 1];
+  int64_t goff[ROUNDS > 0 ? ROUNDS : 1];
+  const int dchunk = (koff % KROW);      // byte offset of the lane's chunk inside its row
+  if constexpr (GKV) {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) dslot[i] = (i * 1024 * NW + koff) / KROW;
+  }
+  auto grid_offsets = [&](int kv) {
+    const int o2 = (kv % p.nk2) << p.lk2;
+    const int o1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+    const int o0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int r = dslot[i];
+      const int t = min(o0 + (r >> ksh), p.L0 - 1);
+      const int y = min(o1 + ((r >> p.lk2) & km1), p.L1 - 1);
+      const int x = min(o2 + (r & km2), p.L2 - 1);
+      goff[i] = (int64_t)((t * p.L1 + y) * p.L2 + x) * (int64_t)(tok_stride * 2) + dchunk;
+    }
+  };
+
   // KV-tile indices live in scalar registers: kv_cur is tile j, kv_nxt tile
   // j+1; tile j+2's index is fetched one tile ahead so no wait on it ever
   // sits between a barrier and the next tile's DMA.
   int kv_cur = kv_idx[beg];
   int kv_nxt = beg + 1 < end ? kv_idx[beg + 1] : 0;
-  tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);   // prologue: tile 0 in flight
-  tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
+  if constexpr (GKV) {    // prologue: tile 0 in flight
+    grid_offsets(kv_cur);
+    for (int kb = 0; kb < KB; ++kb) {
+      tile_to_lds_step_off<TILEB, NW, KB>(kbase, goff, lds, wv, kb);
+      tile_to_lds_step_off<TILEB, NW, KB>(vbase, goff, lds + TILEB, wv, kb);
+    }
+  } else {
+    tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);
+    tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
+  }
 
   // One KV tile from LDS: a software pipeline over its 32-key blocks.  S^T of
   // block kb+1 is issued before the exponentials of block kb, and the max /
@@ -179,15 +274,28 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const unsigned char* nk = kbase;
   const unsigned char* nv = vbase;
   lds_u8* nbuf = lds;
-  auto tile_body = [&](const unsigned char* Ks, const unsigned char* Vs, uint64_t vmask, auto bnd) {
+  auto copy_step = [&](lds_u8* nb, int kb) {
+    if constexpr (GKV) {
+      tile_to_lds_step_off<TILEB, NW, KB>(kbase, goff, nb, wv, kb);
+      tile_to_lds_step_off<TILEB, NW, KB>(vbase, goff, nb + TILEB, wv, kb);
+    } else {
+      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nb, wv, kb);
+      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nb + TILEB, wv, kb);
+    }
+  };
+  // The restrict qualifiers state that the stage being read (Ks, Vs) and the
+  // stage the next tile's copy writes (nb) never overlap; the compiler then
+  // knows the in-flight copy cannot feed this tile's LDS reads and issues no
+  // wait on it before them (it cannot see this for the transposing reads).
+  auto tile_body = [&](const unsigned char* __restrict__ Ks, const unsigned char* __restrict__ Vs,
+                       lds_u8* __restrict__ nb, uint64_t vmask, auto bnd) {
     constexpr bool BOUNDARY = decltype(bnd)::value;
     f32x16 s = qk_block<D, KROW>(Ks, 0, krow0, kswz, hh, qr);
     if constexpr (BOUNDARY) apply_mask(s, vmask, 0);
     rescale_if_needed(s, m, l, o, c2, thr);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
-      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
+      copy_step(nb, kb);
       f32x16 sn;
       if (kb + 1 < KB) sn = qk_block<D, KROW>(Ks, kb + 1, krow0, kswz, hh, qr);
       // ---- P = exp2(S c2 - m c2) in bf16; accumulator i <-> key 16*(i/8) + 8*hh + i%8
@@ -209,8 +317,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
       for (int c = 0; c < 2; ++c) {
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8*>(Vs + (d * 32 + lq) * VROW + (((4 * kb + 2 * c + hh) ^ vswz) * 16));
+          bf16x8 a;
+          if constexpr (GKV) {
+            a = v_operand_tr<D>(Vs, 32 * kb + 16 * c, d, lane);
+          } else {
+            a = *reinterpret_cast<const bf16x8*>(Vs + (d * 32 + lq) * VROW + (((4 * kb + 2 * c + hh) ^ vswz) * 16));
+          }
           o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pv[c], o[d], 0, 0, 0);
         }
       }
@@ -230,8 +342,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     __syncthreads();
     const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
     nbuf = lds + (stage ^ 1) * STAGE;
-    nk = kbase + (size_t)kv_copy * TILEB;
-    nv = vbase + (size_t)kv_copy * TILEB;
+    if constexpr (GKV) {
+      grid_offsets(kv_copy);
+    } else {
+      nk = kbase + (size_t)kv_copy * TILEB;
+      nv = vbase + (size_t)kv_copy * TILEB;
+    }
     const int kv = kv_cur;
     kv_cur = kv_nxt;
     if (j + 2 < end) kv_nxt = kv_idx[j + 2];
@@ -248,15 +364,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     for (int j = beg; j < end; ++j) {
       begin_tile(j, Ks, Vs);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
-        tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
-      }
+      for (int kb = 0; kb < KB; ++kb) copy_step(nbuf, kb);
     }
   } else {
     for (int j = beg; j < beg + nfull; ++j) {
       begin_tile(j, Ks, Vs);
-      tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
+      tile_body(Ks, Vs, nbuf, 0ull, std::integral_constant<bool, false>{});
     }
     for (int j = beg + nfull; j < end; ++j) {
       const int kv = begin_tile(j, Ks, Vs);
@@ -265,7 +378,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
       const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
       const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1, st2, p.w0,
                                                      p.w1, p.w2, p.lk2, km1, km2, ksh);
-      tile_body(Ks, Vs, vmask, std::integral_constant<bool, true>{});
+      tile_body(Ks, Vs, nbuf, vmask, std::integral_constant<bool, true>{});
     }
   }
   // the last step's copy must land before the workgroup's LDS is released
@@ -275,7 +388,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   // padding-only waves store zeros (finite, meaningless rows)
   const float lt = wave_active ? xhalf_sum(l) : 1.f;
   const float inv = 1.f / lt;
-  __bf16* orow = static_cast<__bf16*>(p.ot) + (qtile * QT + row) * D;
+  __bf16* orow = static_cast<__bf16*>(p.ot) + (GQ ? grid_base + (size_t)q_tok * tok_stride : (qtile * QT + row) * D);
+  if (GQ && !q_valid) return;            // padding rows have no place in grid order
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -288,12 +402,19 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
       *reinterpret_cast<bf16x4*>(orow + d * 32 + 8 * g + 4 * hh) = v;
     }
   }
-  if (p.lse_t && hh == 0) p.lse_t[qtile * QT + row] = (m == -INFINITY ? 0.f : m * p.scale) + logf(lt);
+  if (p.lse_t && hh == 0)
+    p.lse_t[GQ ? (grid_base / D) + (size_t)q_tok * p.heads : qtile * QT + row] =
+        (m == -INFINITY ? 0.f : m * p.scale) + logf(lt);
 }
 
 template <int D, int NW, int KVT>
-hipError_t launch_cfg(const KParams& p, hipStream_t st) {
-  attn_bf16_kernel<D, NW, KVT><<<p.num_wg, NW * 64, 0, st>>>(p);
+hipError_t launch_cfg(const KParams& p, int io, hipStream_t st) {
+  if (io == IO_GRID)
+    attn_bf16_kernel<D, NW, KVT, IO_GRID><<<p.num_wg, NW * 64, 0, st>>>(p);
+  else if (io == IO_QO)
+    attn_bf16_kernel<D, NW, KVT, IO_QO><<<p.num_wg, NW * 64, 0, st>>>(p);
+  else
+    attn_bf16_kernel<D, NW, KVT, IO_TILE><<<p.num_wg, NW * 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -307,6 +428,8 @@ bool attn_bf16_supported(int head_dim, int q_tokens, int kv_tokens) {
 // Extra shape rule of the boundary mask: the KV tile's W extent is >= 8.
 bool attn_bf16_tile_ok(const int tile_kv[3]) { return tile_kv[2] >= 8; }
 
+bool attn_bf16_grid_io_supported(int head_dim) { return head_dim == 64 || head_dim == 128; }
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   const KParams p = make_kparams(a);
   const int qtok = a.tq[0] * a.tq[1] * a.tq[2];
@@ -314,14 +437,14 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (!attn_bf16_supported(a.head_dim, qtok, ktok) || !attn_bf16_tile_ok(a.tkv)) return hipErrorInvalidValue;
   const int key = (a.head_dim == 128 ? 4 : 0) | (qtok == 256 ? 2 : 0) | (ktok == 128 ? 1 : 0);
   switch (key) {
-    case 0: return launch_cfg<64, 4, 64>(p, st);
-    case 1: return launch_cfg<64, 4, 128>(p, st);
-    case 2: return launch_cfg<64, 8, 64>(p, st);
-    case 3: return launch_cfg<64, 8, 128>(p, st);
-    case 4: return launch_cfg<128, 4, 64>(p, st);
-    case 5: return launch_cfg<128, 4, 128>(p, st);
-    case 6: return launch_cfg<128, 8, 64>(p, st);
-    default: return launch_cfg<128, 8, 128>(p, st);
+    case 0: return launch_cfg<64, 4, 64>(p, a.io_mode, st);
+    case 1: return launch_cfg<64, 4, 128>(p, a.io_mode, st);
+    case 2: return launch_cfg<64, 8, 64>(p, a.io_mode, st);
+    case 3: return launch_cfg<64, 8, 128>(p, a.io_mode, st);
+    case 4: return launch_cfg<128, 4, 64>(p, a.io_mode, st);
+    case 5: return launch_cfg<128, 4, 128>(p, a.io_mode, st);
+    case 6: return launch_cfg<128, 8, 64>(p, a.io_mode, st);
+    default: return launch_cfg<128, 8, 128>(p, a.io_mode, st);
   }
 }
 

@@ -33,6 +33,7 @@ struct KParams {
   float scale;          // multiplies q.k
   float c2;             // scale * log2(e)
   float v_scale;        // multiplies the output (fp8), else 1
+  int heads;            // heads (grid-order addressing)
 };
 
 inline int host_lg2(int x) {
@@ -64,6 +65,7 @@ inline KParams make_kparams(const AttnArgs& a) {
   p.scale = a.scale;
   p.c2 = a.scale * 1.4426950408889634f;
   p.v_scale = a.v_scale;
+  p.heads = a.heads;
   return p;
 }
 

@@ -14,12 +14,19 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // 16-byte chunk swizzle of a tile row with CPR chunks: chunk c of row r is
 // stored at position c ^ swz(r).  The 64 LDS banks (4 bytes each) span 256
-// bytes = 16 / CPR rows; XOR-ing with the row's index in units of that span
-// sends the same logical chunk of 16 consecutive rows to 16 different bank
-// groups, so a wave's 16-byte reads down a column are conflict-free.
+// bytes = 16 / CPR rows.  Two read shapes must be conflict-free:
+//  * 16-byte reads down a column (16 consecutive rows, one chunk): needs
+//    swz to be a bijection of the row's index within 16 rows (in units of
+//    the 256-byte span) onto the span's 16 chunk slots;
+//  * transposing 8-byte reads (4 consecutive rows x 4 consecutive chunks
+//    each): needs the 4 rows to move the chunk quad to 4 different quads.
+// For CPR = 16 the row's two low bits XOR the chunk's quad bits and the next
+// two XOR the chunk within the quad; for CPR = 8 the same holds after the
+// row pair (two rows share one span) is taken as the unit.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (CPR >= 16) return row & 15;
+  if constexpr (CPR >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (CPR == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
   else return (row / (16 / CPR)) & (CPR - 1);
 }
 

@@ -8,6 +8,10 @@
 
 namespace na {
 
+// Layouts of the attention kernel's tensors: all in tile order; q / out / lse
+// in grid order with k / v in tile order; all in grid order.
+enum IoMode { IO_TILE = 0, IO_QO = 1, IO_GRID = 2 };
+
 struct AttnArgs {
   const void* qt;          // q, tile order (tile_q tiles)
   const void* kt;          // k, tile order (tile_kv tiles)
@@ -23,6 +27,7 @@ struct AttnArgs {
   int nq[3], nk[3];        // tiles per axis
   float scale;             // multiplies q.k (fp8: includes the q and k scales)
   float v_scale;           // fp8: multiplies the output; else 1
+  int io_mode;             // IO_TILE, IO_QO or IO_GRID (tensor layouts, see attn_bf16.hip)
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
@@ -35,6 +40,8 @@ bool attn_fp8_supported(int head_dim, int q_tokens, int kv_tokens);
 bool attn_f32_supported(int head_dim, int q_tokens, int kv_tokens);
 // The bf16/fp8 kernels need KV tiles at least 8 tokens wide along W.
 bool attn_bf16_tile_ok(const int tile_kv[3]);
+// Whether the bf16 kernel can read and write grid order directly.
+bool attn_bf16_grid_io_supported(int head_dim);
 
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
 size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);

@@ -149,6 +149,7 @@ struct Layout {
   int nq[3], nk[3];
   size_t q_bytes, kv_bytes, o_bytes, lse_bytes;
   size_t off_q, off_k, off_v, off_o, off_lse, total;
+  size_t kv_total;   // k and v copies only (offsets 0 and round256(kv_bytes))
 };
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -191,7 +192,19 @@ na_status check_problem(int batch, int heads, int head_dim, const int grid[3], c
   lay->off_o = lay->off_v + round256(lay->kv_bytes);
   lay->off_lse = lay->off_o + round256(lay->o_bytes);
   lay->total = lay->off_lse + round256(lay->lse_bytes);
+  lay->kv_total = 2 * round256(lay->kv_bytes);
   return NA_OK;
+}
+
+// Which form na_forward takes (the values of na_forward_mode): 0 permutes q,
+// k, v and unpermutes out, lse; 1 permutes k, v only (bf16: the kernel reads q
+// and writes out / lse in grid order); 2 permutes nothing (bf16 without a
+// workspace).  Test hook: NA_NO_FUSED=1 forces form 0.
+int forward_mode(na_dtype dt, int head_dim, bool with_workspace) {
+  const char* e = std::getenv("NA_NO_FUSED");
+  if (e && e[0] == '1') return 0;
+  if (dt != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim)) return 0;
+  return with_workspace ? 1 : 2;
 }
 
 na_status hip_status(hipError_t e, const char* what) {
@@ -278,7 +291,12 @@ size_t na_workspace_bytes(int batch, int heads, int head_dim, const int grid[3],
   g_err.clear();
   Layout lay;
   if (check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay) != NA_OK) return 0;
+  if (lay.total && forward_mode(dtype, head_dim, true) == 1) return lay.kv_total;
   return lay.total;
+}
+
+int na_forward_mode(na_dtype dtype, int head_dim, int with_workspace) {
+  return forward_mode(dtype, head_dim, with_workspace != 0);
 }
 
 na_status na_permute(const void* x, void* xt, int batch, int heads, int head_dim, const int grid[3],
@@ -331,7 +349,7 @@ na_status na_unpermute_lse(const float* lse_t, float* lse, int batch, int heads,
 static na_status attend_impl(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
                              int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
                              const Layout& lay, float scale, na_dtype dtype, const float* qkv_scale,
-                             hipStream_t stream) {
+                             int io_mode, hipStream_t stream) {
   na::Geometry g = make_geom(grid, window, stride);
   Plan* plan = nullptr;
   na_status st = get_plan(g, lay.tq, lay.tkv, &plan);
@@ -359,6 +377,7 @@ static na_status attend_impl(const void* qt, const void* kt, const void* vt, voi
   }
   a.scale = scale;
   a.v_scale = 1.0f;
+  a.io_mode = io_mode;
   if (dtype == NA_FP8_E4M3 && qkv_scale) {
     a.scale = scale * qkv_scale[0] * qkv_scale[1];
     a.v_scale = qkv_scale[2];
@@ -402,7 +421,30 @@ na_status na_attend_tiled(const void* qt, const void* kt, const void* vt, void* 
   st = check_scales(scale, dtype, qkv_scale);
   if (st != NA_OK) return st;
   return attend_impl(qt, kt, vt, ot, lse_t, batch, heads, head_dim, grid, window, stride, lay, scale, dtype,
-                     qkv_scale, (hipStream_t)stream);
+                     qkv_scale, na::IO_TILE, (hipStream_t)stream);
+}
+
+na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt, void* out, float* lse, int batch,
+                             int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                             const int tile_kv[3], float scale, na_dtype dtype, void* stream) {
+  g_err.clear();
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (!tile_kv) return fail(NA_ERR_INVALID_ARG, "tile_kv must be non-null");
+  for (int d = 0; d < 3; ++d)
+    if (tile_kv[d] != lay.tkv[d]) return fail(NA_ERR_INVALID_ARG, "tile_kv differs from na_choose_tiles()");
+  if (dtype != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim))
+    return fail(NA_ERR_UNSUPPORTED, "grid-order q / out need bf16 with head_dim 64 or 128");
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!q || !kt || !vt || !out) return fail(NA_ERR_INVALID_ARG, "q, kt, vt and out must be non-null");
+  if (!aligned16(q) || !aligned16(kt) || !aligned16(vt) || !aligned16(out))
+    return fail(NA_ERR_INVALID_ARG, "q, kt, vt and out must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  st = check_scales(scale, dtype, nullptr);
+  if (st != NA_OK) return st;
+  return attend_impl(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, lay, scale, dtype, nullptr,
+                     na::IO_QO, (hipStream_t)stream);
 }
 
 na_status na_forward(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int heads,
@@ -418,12 +460,20 @@ na_status na_forward(const void* q, const void* k, const void* v, void* out, flo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if (!workspace) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null");
-  if (!aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if (workspace_bytes < lay.total)
-    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(lay.total) + " bytes");
   st = check_scales(scale, dtype, qkv_scale);
   if (st != NA_OK) return st;
+  const int mode = forward_mode(dtype, head_dim, workspace != nullptr);
+  if (mode == 2) {
+    // no workspace: the kernel gathers K / V tiles from grid order and reads
+    // and writes q, out, lse in place (no permutation pass)
+    return attend_impl(q, k, v, out, lse, batch, heads, head_dim, grid, window, stride, lay, scale, dtype,
+                       qkv_scale, na::IO_GRID, (hipStream_t)stream);
+  }
+  if (!workspace) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null for this dtype / head_dim");
+  if (!aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t need = mode == 1 ? lay.kv_total : lay.total;
+  if (workspace_bytes < need)
+    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
   if ((head_dim * elem_bytes(dtype)) % 16 != 0 || (head_dim * out_bytes(dtype)) % 16 != 0)
     return fail(NA_ERR_UNSUPPORTED, "head_dim too small for 16-byte rows");
   // Make sure the plan exists before anything is enqueued, so a failing
@@ -433,14 +483,25 @@ na_status na_forward(const void* q, const void* k, const void* v, void* out, flo
   if (st != NA_OK) return st;
 
   char* ws = static_cast<char*>(workspace);
+  const int eb = elem_bytes(dtype);
+  const int vtrans = dtype == NA_F32 ? 0 : 1;
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == 1) {
+    void* kt = ws;
+    void* vt = ws + round256(lay.kv_bytes);
+    if ((st = hip_status(na::launch_permute(k, kt, batch, heads, head_dim, grid, lay.tkv, eb, 0, s), "permute k")))
+      return st;
+    if ((st = hip_status(na::launch_permute(v, vt, batch, heads, head_dim, grid, lay.tkv, eb, vtrans, s),
+                         "permute v")))
+      return st;
+    return attend_impl(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, lay, scale, dtype,
+                       qkv_scale, na::IO_QO, s);
+  }
   void* qt = ws + lay.off_q;
   void* kt = ws + lay.off_k;
   void* vt = ws + lay.off_v;
   void* ot = ws + lay.off_o;
   float* lt = reinterpret_cast<float*>(ws + lay.off_lse);
-  const int eb = elem_bytes(dtype);
-  const int vtrans = dtype == NA_F32 ? 0 : 1;
-  hipStream_t s = (hipStream_t)stream;
   if ((st = hip_status(na::launch_permute(q, qt, batch, heads, head_dim, grid, lay.tq, eb, 0, s), "permute q")))
     return st;
   if ((st = hip_status(na::launch_permute(k, kt, batch, heads, head_dim, grid, lay.tkv, eb, 0, s), "permute k")))
@@ -449,7 +510,7 @@ na_status na_forward(const void* q, const void* k, const void* v, void* out, flo
                        "permute v")))
     return st;
   st = attend_impl(qt, kt, vt, ot, lse ? lt : nullptr, batch, heads, head_dim, grid, window, stride, lay, scale,
-                   dtype, qkv_scale, s);
+                   dtype, qkv_scale, na::IO_TILE, s);
   if (st != NA_OK) return st;
   if ((st = hip_status(na::launch_unpermute(ot, out, batch, heads, head_dim, grid, lay.tq, out_bytes(dtype), s),
                        "unpermute out")))

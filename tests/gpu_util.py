@@ -23,9 +23,15 @@ def say(*a):
     sys.stdout.flush()
 
 
+# whether run_hip passes a workspace to na_forward (bf16: False selects the
+# form that permutes nothing); the `path` fixtures switch it
+USE_WORKSPACE = True
+
+
 def run_hip(na, wl, q, k, v, sc, window=None, stride=None):
     f = na.Forward(q, k, v, window or wl.window, stride or wl.stride, scale=wl.scale,
-                   qkv_scale=sc if wl.dtype == "fp8" else None)
+                   qkv_scale=sc if wl.dtype == "fp8" else None,
+                   workspace=USE_WORKSPACE or wl.dtype != "bf16" or q.shape[-1] not in (64, 128))
     out, lse = f()
     torch.cuda.synchronize()
     return out, lse, f
@@ -54,6 +60,17 @@ def compare(wl, qc, kc, vc, sc, out, lse, queries=None, heads=None, window=None,
         eo = max(eo, float(np.abs(go - ro[:, :, 0, :]).max()))
         el = max(el, float(np.abs(gl - rl[:, :, 0]).max()))
     return eo, el
+
+
+def set_path(monkeypatch, path):
+    """Selects the form of na_forward: "qo" (default: k, v permuted; q, out,
+    lse in grid order), "grid" (no permutation, no workspace) or "tiled"
+    (q, k, v permuted, out / lse unpermuted)."""
+    import gpu_util
+    if path == "tiled":
+        monkeypatch.setenv("NA_NO_FUSED", "1")
+    if path == "grid":
+        monkeypatch.setattr(gpu_util, "USE_WORKSPACE", False)
 
 
 def inputs(wl):

@@ -83,8 +83,11 @@ def test_chosen_tiles_video_block_are_perfectly_aligned(na):
     assert st["nnz"] == st["n_q_tiles"] * 81
 
 
-def test_workspace_is_linear_in_tokens(na):
-    # no N x N buffer: doubling the grid doubles the workspace (up to padding)
+@pytest.mark.parametrize("no_fused", ["1", "0"])
+def test_workspace_is_linear_in_tokens(na, monkeypatch, no_fused):
+    # no N x N buffer: doubling the grid doubles the workspace (up to padding),
+    # for both the all-copies form and the k / v-copies form
+    monkeypatch.setenv("NA_NO_FUSED", no_fused)
     a = na.na_workspace_bytes(1, 2, 128, (1, 64, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
     b = na.na_workspace_bytes(1, 2, 128, (1, 128, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
     assert 1.9 < b / a < 2.1
@@ -96,7 +99,30 @@ def _status(na, fn, *args):
     return getattr(na.load(), fn)(*args)
 
 
-def test_invalid_arguments_rejected(na):
+def test_forward_mode_rule(na, monkeypatch):
+    for D in (64, 128):
+        assert na.na_forward_mode(na.NA_BF16, D, True) == 1
+        assert na.na_forward_mode(na.NA_BF16, D, False) == 2
+    assert na.na_forward_mode(na.NA_BF16, 32, True) == 0
+    for dt in (na.NA_F32, na.NA_FP8_E4M3):
+        assert na.na_forward_mode(dt, 128, True) == 0 and na.na_forward_mode(dt, 128, False) == 0
+    monkeypatch.setenv("NA_NO_FUSED", "1")
+    assert na.na_forward_mode(na.NA_BF16, 128, True) == 0 and na.na_forward_mode(na.NA_BF16, 128, False) == 0
+
+
+def test_kv_copy_form_workspace(na, monkeypatch):
+    # form 1 holds exactly the k and v tile copies: 2 x B x H x padded tokens x D x 2 bytes
+    grid, window, stride = (1, 64, 64), (1, 9, 9), (1, 1, 1)
+    tq, tk = na.na_choose_tiles(grid, window, stride, 128, na.NA_BF16)
+    padded = math.prod(-(-L // t) * t for L, t in zip(grid, tk))
+    kv = 1 * 2 * padded * 128 * 2
+    assert na.na_workspace_bytes(1, 2, 128, grid, window, stride, na.NA_BF16) == 2 * ((kv + 255) // 256 * 256)
+    monkeypatch.setenv("NA_NO_FUSED", "1")
+    assert na.na_workspace_bytes(1, 2, 128, grid, window, stride, na.NA_BF16) > 2 * kv
+
+
+def test_invalid_arguments_rejected(na, monkeypatch):
+    monkeypatch.setenv("NA_NO_FUSED", "1")   # the workspace checks belong to the permute path
     lib = na.load()
     I3 = na.I3
     good = dict(grid=I3(1, 16, 16), window=I3(1, 5, 5), stride=I3(1, 1, 1))
@@ -116,11 +142,20 @@ def test_invalid_arguments_rejected(na):
     assert fwd(q=None) == na.NA_ERR_INVALID_ARG                        # null pointer
     assert fwd(out=fake + 8) == na.NA_ERR_INVALID_ARG                  # misaligned
     assert fwd(ws_bytes=ws - 1) == na.NA_ERR_WORKSPACE
+    assert fwd(dt=na.NA_F32, D=32, ws_ptr=None) == na.NA_ERR_INVALID_ARG   # fp32 needs a workspace
     assert fwd(D=48) == na.NA_ERR_UNSUPPORTED
     assert fwd(dt=7) == na.NA_ERR_INVALID_ARG
     assert fwd(scale=float("nan")) == na.NA_ERR_INVALID_ARG
     assert fwd(scale=-0.5) == na.NA_ERR_INVALID_ARG
     assert "scale" in na.na_last_error()
+    # the form-1 kernel entry point: bf16 only, tile_kv checked
+    tk = na.I3(*na.na_choose_tiles((1, 16, 16), (1, 5, 5), (1, 1, 1), 64, na.NA_BF16)[1])
+    assert lib.na_attend_kv_tiled(fake, fake, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
+                                  good["stride"], tk, 0.125, na.NA_FP8_E4M3, None) == na.NA_ERR_UNSUPPORTED
+    assert lib.na_attend_kv_tiled(fake, fake, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
+                                  good["stride"], I3(1, 1, 1), 0.125, na.NA_BF16, None) == na.NA_ERR_INVALID_ARG
+    assert lib.na_attend_kv_tiled(fake, None, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
+                                  good["stride"], tk, 0.125, na.NA_BF16, None) == na.NA_ERR_INVALID_ARG
     # permutation kernels
     assert lib.na_permute(fake, fake, 1, 1, 64, I3(1, 16, 16), I3(1, 3, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG
     assert lib.na_permute(fake, None, 1, 1, 64, I3(1, 16, 16), I3(1, 8, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG

@@ -9,16 +9,23 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, compare, inputs, run_hip, say
+from gpu_util import TOL, compare, inputs, run_hip, say, set_path
 from synth import WORKLOADS, sample_queries
 
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["qo", "grid", "tiled"])
+def path(request, monkeypatch):
+    """The three forms of the bf16 forward (see gpu_util.set_path)."""
+    set_path(monkeypatch, request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("name", ["img16_f32", "img64_sliding", "img64_block"])
-def test_small_workloads_all_queries(na, name):
+def test_small_workloads_all_queries(na, name, path):
     wl = WORKLOADS[name]
-    say(f"[parity] {name} grid={wl.grid} w={wl.window} s={wl.stride} D={wl.head_dim} {wl.dtype}")
+    say(f"[parity] {name} ({path}) grid={wl.grid} w={wl.window} s={wl.stride} D={wl.head_dim} {wl.dtype}")
     qc, kc, vc, sc, q, k, v = inputs(wl)
     out, lse, _ = run_hip(na, wl, q, k, v, sc)
     eo, el = compare(wl, qc, kc, vc, sc, out, lse)
@@ -29,7 +36,9 @@ def test_small_workloads_all_queries(na, name):
 
 @pytest.mark.parametrize("name,heads", [("video_block", (0, 23)), ("video_sliding", (5,)),
                                         ("img256_block", (0, 17)), ("img256_block_fp8", (3, 20))])
-def test_full_size_sampled(na, name, heads):
+def test_full_size_sampled(na, name, heads, path):
+    if path == "tiled" and name != "video_block":
+        pytest.skip("the tiled bf16 path at full size is covered by the video block workload")
     wl = WORKLOADS[name]
     qc, kc, vc, sc, q, k, v = inputs(wl)
     tq, _ = na.na_choose_tiles(wl.grid, wl.window, wl.stride, wl.head_dim, na.dtype_code(q.dtype))
@@ -57,12 +66,12 @@ VARIANTS = [
 
 @pytest.mark.parametrize("tq,tk", VARIANTS)
 @pytest.mark.parametrize("D", [64, 128])
-def test_kernel_variants_ragged_grid(na, monkeypatch, tq, tk, D):
+def test_kernel_variants_ragged_grid(na, monkeypatch, tq, tk, D, path):
     wl = WORKLOADS["video_sliding"].with_(name="ragged", batch=2, heads=3, grid=(5, 19, 27), head_dim=D,
                                           window=(3, 7, 9), stride=(1, 2, 3), seed=777)
     monkeypatch.setenv("NA_TILE_Q", tq)
     monkeypatch.setenv("NA_TILE_KV", tk)
-    say(f"[parity] variant tq={tq} tk={tk} D={D} grid={wl.grid}")
+    say(f"[parity] variant ({path}) tq={tq} tk={tk} D={D} grid={wl.grid}")
     qc, kc, vc, sc, q, k, v = inputs(wl)
     out, lse, f = run_hip(na, wl, q, k, v, sc)
     assert f.tile_q == tuple(int(x) for x in tq.split(","))

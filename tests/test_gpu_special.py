@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import TOL, compare, inputs, run_hip, say
+from gpu_util import TOL, compare, inputs, run_hip, say, set_path
 from synth import WORKLOADS, make_qkv, to_f64
 
 pytestmark = pytest.mark.gpu
@@ -51,14 +51,23 @@ def test_permute_layout_and_round_trip(na, dtype, tile, transpose):
 
 
 def _run(na, wl, q, k, v, window=None, stride=None):
-    f = na.Forward(q, k, v, window or wl.window, stride or wl.stride, scale=wl.scale)
+    import gpu_util
+    ws = gpu_util.USE_WORKSPACE or q.dtype != torch.bfloat16 or q.shape[-1] not in (64, 128)
+    f = na.Forward(q, k, v, window or wl.window, stride or wl.stride, scale=wl.scale, workspace=ws)
     out, lse = f()
     torch.cuda.synchronize()
     return out, lse
 
 
+@pytest.fixture(params=["qo", "grid", "tiled"])
+def path(request, monkeypatch):
+    """The three forms of the bf16 forward (see gpu_util.set_path)."""
+    set_path(monkeypatch, request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_window_one_returns_v_exactly(na, dtype):
+def test_window_one_returns_v_exactly(na, dtype, path):
     wl = WORKLOADS["img64_block"].with_(grid=(3, 17, 20), window=(1, 1, 1), stride=(1, 1, 1), dtype=dtype,
                                         head_dim=64, heads=2, seed=91)
     say(f"[special] window 1 {dtype}")
@@ -69,7 +78,7 @@ def test_window_one_returns_v_exactly(na, dtype):
     assert float((lse.cpu().double() - ref).abs().max()) <= TOL[dtype][1]
 
 
-def test_zero_queries_give_window_mean(na):
+def test_zero_queries_give_window_mean(na, path):
     wl = WORKLOADS["img64_block"].with_(grid=(2, 21, 18), window=(2, 6, 5), stride=(1, 3, 2), heads=2, seed=92)
     say("[special] q = 0")
     qc, kc, vc, sc, q, k, v = inputs(wl)
@@ -81,7 +90,7 @@ def test_zero_queries_give_window_mean(na):
 
 
 @pytest.mark.parametrize("stride", [(1, 1, 1), (2, 3, 4)])
-def test_window_equal_grid_is_dense(na, stride):
+def test_window_equal_grid_is_dense(na, stride, path):
     wl = WORKLOADS["img64_block"].with_(grid=(2, 12, 16), window=(2, 12, 16), stride=stride, heads=2,
                                         head_dim=128, seed=93)
     say(f"[special] window = grid, stride {stride}")
@@ -92,7 +101,7 @@ def test_window_equal_grid_is_dense(na, stride):
     assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
 
 
-def test_stride_equal_window_is_block_diagonal(na):
+def test_stride_equal_window_is_block_diagonal(na, path):
     wl = WORKLOADS["img64_block"].with_(grid=(4, 24, 32), window=(2, 8, 8), stride=(2, 8, 8), heads=2,
                                         head_dim=128, seed=94)
     say("[special] stride = window")
@@ -121,7 +130,7 @@ def test_translation_equivariance_sliding(na):
     assert float((ia - ib).abs().max()) <= 2 * TOL["bf16"][0]
 
 
-def test_forced_mask_on_full_tiles_is_bit_identical(na, monkeypatch):
+def test_forced_mask_on_full_tiles_is_bit_identical(na, monkeypatch, path):
     # GNA page section 2.1: the mask is only needed on boundary tiles; applying
     # it to full tiles too must not change a single bit
     wl = WORKLOADS["video_block"].with_(grid=(20, 24, 32), heads=2, seed=96)
@@ -133,14 +142,16 @@ def test_forced_mask_on_full_tiles_is_bit_identical(na, monkeypatch):
     assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
 
 
-def test_every_output_written(na):
+def test_every_output_written(na, path):
     wl = WORKLOADS["video_sliding"].with_(grid=(3, 13, 21), window=(3, 5, 7), heads=3, seed=97)
     say("[special] poisoned outputs")
     qc, kc, vc, sc, q, k, v = inputs(wl)
-    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale)
+    import gpu_util
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=gpu_util.USE_WORKSPACE)
     f.out.fill_(float("nan"))
     f.lse.fill_(float("nan"))
-    f.workspace.fill_(0xFF)   # NaN patterns in every tile-order buffer
+    if f.workspace is not None:
+        f.workspace.fill_(0xFF)   # NaN patterns in every tile-order buffer
     out, lse = f()
     torch.cuda.synchronize()
     assert torch.isfinite(out).all() and torch.isfinite(lse).all()
@@ -148,20 +159,22 @@ def test_every_output_written(na):
     assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
 
 
-def test_no_lse_and_empty_batch(na):
+def test_no_lse_and_empty_batch(na, path):
     wl = WORKLOADS["img64_sliding"].with_(heads=2, seed=98)
     qc, kc, vc, sc, q, k, v = inputs(wl)
     say("[special] lse = NULL, empty batch")
-    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, return_lse=False)
+    import gpu_util
+    ws = gpu_util.USE_WORKSPACE
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, return_lse=False, workspace=ws)
     out, lse = f()
     torch.cuda.synchronize()
     assert lse is None
-    f2 = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale)
+    f2 = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=ws)
     out2, _ = f2()
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
     e = torch.empty((0, 1, 64, 64, 2, 64), dtype=torch.bfloat16, device="cuda")
-    o, l = na.forward(e, e, e, (1, 17, 17), (1, 1, 1))
+    o, l = na.forward(e, e, e, (1, 17, 17), (1, 1, 1), workspace=ws)
     assert o.shape == e.shape and l.shape == e.shape[:-1]
 
 
@@ -177,3 +190,20 @@ def test_fp8_window_one_returns_scaled_v_exactly(na):
     assert torch.equal(out.cpu(), ref)
     lref = wl.scale * sc[0] * sc[1] * (qc.double() * kc.double()).sum(-1)
     assert float((lse.cpu().double() - lref).abs().max()) <= TOL["fp8"][1]
+
+
+@pytest.mark.parametrize("grid", [(20, 24, 40), (5, 19, 27)])
+def test_three_forward_forms_agree(na, monkeypatch, grid):
+    # the three forms feed the same tiles to the same arithmetic in the same
+    # order: results are bit-identical (ragged grid: padding handled alike)
+    wl = WORKLOADS["video_block"].with_(grid=grid, window=(3, 7, 9) if grid[0] == 5 else (18, 24, 24),
+                                        stride=(1, 2, 3) if grid[0] == 5 else (16, 8, 8), heads=2, seed=100)
+    say(f"[special] three forms agree grid={grid}")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    res = {}
+    for form in ("qo", "grid", "tiled"):
+        with monkeypatch.context() as m:
+            set_path(m, form)
+            res[form] = _run(na, wl, q, k, v)
+    for form in ("grid", "tiled"):
+        assert torch.equal(res["qo"][0], res[form][0]) and torch.equal(res["qo"][1], res[form][1]), form
