@@ -155,7 +155,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   lds_u8* lds = (lds_u8*)smem;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6, hh = lane >> 5, lq = lane & 31;
+  // wv is wave-uniform: keeping it in a scalar register lets the LDS-DMA
+  // destination (M0) be computed with scalar arithmetic
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), hh = lane >> 5, lq = lane & 31;
   const WorkItem wi = decode_work(p, blockIdx.x);
   const size_t qtile = (size_t)wi.bh * p.nQ + wi.qrow;
   const int row = wv * 32 + lq;          // this lane's query inside the Q tile

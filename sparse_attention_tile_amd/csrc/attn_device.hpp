@@ -59,7 +59,7 @@ __device__ __forceinline__ int dma_lane_offset(int wv, int lane) {
 }
 
 template <int TILEB, int NW>
-__device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds, int wv) {
+__device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g, unsigned lane_off, lds_u8* lds, int wv) {
   constexpr int ROUND = 1024 * NW;
   static_assert(TILEB % ROUND == 0, "tile must split evenly over the waves");
 #pragma unroll
@@ -73,8 +73,8 @@ __device__ __forceinline__ void tile_to_lds(const unsigned char* __restrict__ g,
 // memory path sees a steady trickle instead of every wave's whole copy at
 // the barrier (which would stall all waves until the address queue drains).
 template <int TILEB, int NW, int KB>
-__device__ __forceinline__ void tile_to_lds_step(const unsigned char* __restrict__ g, int lane_off, lds_u8* lds,
-                                                 int wv, int kb) {
+__device__ __forceinline__ void tile_to_lds_step(const unsigned char* __restrict__ g, unsigned lane_off,
+                                                 lds_u8* lds, int wv, int kb) {
   constexpr int ROUND = 1024 * NW;
   constexpr int ROUNDS = TILEB / ROUND;
 #pragma unroll
