@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_block")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="run the workload's geometry at another head_dim (synthetic inputs of that shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -146,6 +148,8 @@ def main():
     from synth import WORKLOADS, make_qkv
 
     wl = WORKLOADS[args.workload]
+    if args.head_dim is not None and args.head_dim != wl.head_dim:
+        wl = wl.with_(name=f"{wl.name}_d{args.head_dim}", head_dim=args.head_dim)
     qc, kc, vc, sc = make_qkv(wl, device="cpu")
     q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
     fp8 = wl.dtype == "fp8"
@@ -264,6 +268,15 @@ def main():
             "computed_over_effective_flops": computed / eff,
             "kernel_source_sha256_16": src_hash,
         },
+    }
+
+    # the analytic model's prediction for the same problem, beside the measurement
+    sim = na.na_simulate(B, H, D, wl.grid, wl.window, wl.stride, dcode)
+    result["model"] = {
+        "predicted_kernel_ms": sim["predicted_kernel_ms"], "measured_kernel_ms": kernel_ms,
+        "predicted_forward_ms": sim["predicted_forward_ms"], "measured_forward_ms": ms,
+        "tile_efficiency": sim["tile_efficiency"], "perfectly_block_sparse": sim["perfectly_block_sparse"],
+        "speedup_bound_vs_dense": sim["speedup_bound"], "flop_ratio_vs_dense": sim["flop_ratio_vs_dense"],
     }
 
     if not args.no_dense and wl.name == "video_block":

@@ -88,6 +88,29 @@ typedef struct na_tilemap_stats {
   int64_t effective_slots;
 } na_tilemap_stats;
 
+/* One tile-shape configuration as the analytic model sees it. */
+typedef struct na_sim_result {
+  int32_t tile_q[3];
+  int32_t tile_kv[3];
+  na_tilemap_stats stats;        /* per (batch, head)                       */
+  double tile_efficiency;        /* effective / computed slots              */
+  double flop_ratio_vs_dense;    /* N / prod(window): FLOPs of the dense call
+                                    over FLOPs of this one                  */
+  double speedup_bound;          /* computed slots of the dense call (window
+                                    = grid, its own tiles) over computed slots
+                                    of this one: the speedup over dense that
+                                    the tile-level work allows at equal
+                                    per-slot speed                          */
+  int32_t perfectly_block_sparse;/* 1 iff every listed KV tile is full: KV
+                                    tile edges align with every window, no
+                                    key slot is masked (padded query rows,
+                                    counted in tile_efficiency, aside)      */
+  int32_t form;                  /* na_forward_mode with a workspace        */
+  double cost;                   /* the tile chooser's relative cost        */
+  double predicted_kernel_ms;    /* attention kernel on one MI355X          */
+  double predicted_forward_ms;   /* plus the permutations of `form`         */
+} na_sim_result;
+
 /* ---------------------------------------------------------------------- */
 /* Host-only entry points (no HIP call; usable without a GPU).            */
 /* ---------------------------------------------------------------------- */
@@ -124,6 +147,28 @@ na_status na_build_tile_map(const int grid[3], const int window[3],
                             int32_t* kv_idx, int32_t* n_full,
                             int64_t kv_capacity, int64_t* nnz_out,
                             na_tilemap_stats* stats);
+
+/* Analytic model of one problem (GNA page, sections 4.2 and 5: check the
+ * theoretical speedup bound of a configuration with a simulator before
+ * running it, and pick the tiling per hardware).  From the tile map alone it
+ * reports computed vs effective work, whether the configuration is perfectly
+ * block-sparse, the speedup bound over the dense call, and a predicted
+ * MI355X time from a per-CU serial model calibrated on the measured kernels.
+ * tile_q / tile_kv: the shapes to evaluate (powers of two), or both NULL for
+ * the shapes na_choose_tiles picks.  Writes *out (host).  Errors as
+ * na_choose_tiles. */
+na_status na_simulate(int batch, int heads, int head_dim, const int grid[3],
+                      const int window[3], const int stride[3],
+                      na_dtype dtype, const int tile_q[3],
+                      const int tile_kv[3], na_sim_result* out);
+
+/* Every tile-shape pair na_choose_tiles considers for the problem, sorted by
+ * its cost (out[0] is the chosen pair), each evaluated as by na_simulate.
+ * Writes min(count, capacity) entries to out (host; may be NULL when
+ * capacity is 0) and returns the total count, or a negative na_status. */
+int na_tile_candidates(int batch, int heads, int head_dim, const int grid[3],
+                       const int window[3], const int stride[3],
+                       na_dtype dtype, na_sim_result* out, int capacity);
 
 /* Bytes of device workspace na_forward needs for this problem: the
  * tile-ordered copies it makes (form 1 of na_forward_mode: k and v; form 0:

@@ -22,7 +22,8 @@ NA_OK, NA_ERR_INVALID_ARG, NA_ERR_UNSUPPORTED, NA_ERR_WORKSPACE, NA_ERR_HIP = 0,
 NA_F32, NA_BF16, NA_FP8_E4M3 = 0, 1, 2
 
 SYMBOLS = (
-    "na_choose_tiles", "na_build_tile_map", "na_workspace_bytes", "na_forward_mode", "na_last_error",
+    "na_choose_tiles", "na_build_tile_map", "na_simulate", "na_tile_candidates", "na_workspace_bytes",
+    "na_forward_mode", "na_last_error",
     "na_release_cache", "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
     "na_attend_kv_tiled",
 )
@@ -37,6 +38,21 @@ class NAError(RuntimeError):
 class TileMapStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_q_tiles", "n_kv_tiles", "nnz", "n_full", "n_boundary", "computed_slots", "effective_slots")]
+
+
+class SimResult(ctypes.Structure):
+    _fields_ = [("tile_q", ctypes.c_int32 * 3), ("tile_kv", ctypes.c_int32 * 3), ("stats", TileMapStats),
+                ("tile_efficiency", ctypes.c_double), ("flop_ratio_vs_dense", ctypes.c_double),
+                ("speedup_bound", ctypes.c_double), ("perfectly_block_sparse", ctypes.c_int32),
+                ("form", ctypes.c_int32), ("cost", ctypes.c_double), ("predicted_kernel_ms", ctypes.c_double),
+                ("predicted_forward_ms", ctypes.c_double)]
+
+    def as_dict(self):
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        d["tile_q"], d["tile_kv"] = tuple(self.tile_q), tuple(self.tile_kv)
+        d["stats"] = {n: getattr(self.stats, n) for n, _ in TileMapStats._fields_}
+        d["perfectly_block_sparse"] = bool(self.perfectly_block_sparse)
+        return d
 
 
 _lib = None
@@ -60,7 +76,10 @@ def load():
         "na_build_tile_map": ([I3, I3, I3, I3, I3, _p, _p, _p, ctypes.c_int64,
                                ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(TileMapStats)], _i),
         "na_workspace_bytes": ([_i, _i, _i, I3, I3, I3, _i], ctypes.c_size_t),
-        "na_forward_mode": ([_i, _i], _i),
+        "na_forward_mode": ([_i, _i, _i], _i),
+        "na_simulate": ([_i, _i, _i, I3, I3, I3, _i, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                         ctypes.POINTER(SimResult)], _i),
+        "na_tile_candidates": ([_i, _i, _i, I3, I3, I3, _i, ctypes.POINTER(SimResult), _i], _i),
         "na_last_error": ([], ctypes.c_char_p),
         "na_release_cache": ([], None),
         "na_forward": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _fp, _p,
@@ -125,6 +144,31 @@ def na_build_tile_map(grid, window, stride, tile_q, tile_kv):
                                  ctypes.byref(nnz), ctypes.byref(st)))
     stats = {n: getattr(st, n) for n, _ in TileMapStats._fields_}
     return qptr, kv[: nnz.value], nf, stats
+
+
+def na_simulate(batch, heads, head_dim, grid, window, stride, dtype, tile_q=None, tile_kv=None) -> dict:
+    """Analytic model of one problem (see na.h): tile statistics, speedup
+    bound over dense, perfectly-block-sparse flag, predicted MI355X ms."""
+    r = SimResult()
+    tq = _i3(tile_q) if tile_q is not None else None
+    tk = _i3(tile_kv) if tile_kv is not None else None
+    _check(load().na_simulate(batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride), dtype, tq, tk,
+                              ctypes.byref(r)))
+    return r.as_dict()
+
+
+def na_tile_candidates(batch, heads, head_dim, grid, window, stride, dtype) -> list:
+    """Every tile-shape pair the chooser considers, sorted by cost (first =
+    chosen), each as na_simulate reports it."""
+    lib = load()
+    n = lib.na_tile_candidates(batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride), dtype, None, 0)
+    if n < 0:
+        _check(n)
+    arr = (SimResult * max(1, n))()
+    m = lib.na_tile_candidates(batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride), dtype, arr, n)
+    if m < 0:
+        _check(m)
+    return [arr[i].as_dict() for i in range(n)]
 
 
 def na_forward_mode(dtype, head_dim, with_workspace=True) -> int:

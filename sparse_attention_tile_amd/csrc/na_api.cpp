@@ -253,6 +253,91 @@ na_status na_choose_tiles(const int grid[3], const int window[3], const int stri
   return NA_OK;
 }
 
+static void fill_sim(int batch, int heads, int head_dim, const na::Geometry& g, na_dtype dtype, const int tq[3],
+                     const int tkv[3], const na::TileCounts& c, double cost, na_sim_result* r) {
+  for (int d = 0; d < 3; ++d) {
+    r->tile_q[d] = tq[d];
+    r->tile_kv[d] = tkv[d];
+  }
+  r->stats.n_q_tiles = c.n_q_tiles;
+  r->stats.n_kv_tiles = c.n_kv_tiles;
+  r->stats.nnz = c.nnz;
+  r->stats.n_full = c.n_full;
+  r->stats.n_boundary = c.nnz - c.n_full;
+  r->stats.computed_slots = c.computed_slots;
+  r->stats.effective_slots = c.effective_slots;
+  r->tile_efficiency = c.computed_slots ? (double)c.effective_slots / (double)c.computed_slots : 1.0;
+  const double N = (double)g.L[0] * g.L[1] * g.L[2];
+  const double W = (double)g.w[0] * g.w[1] * g.w[2];
+  r->flop_ratio_vs_dense = N / W;
+  // the dense call: window = grid, stride 1, with the tiles it would choose
+  na::Geometry dg = g;
+  for (int d = 0; d < 3; ++d) {
+    dg.w[d] = g.L[d];
+    dg.s[d] = 1;
+  }
+  int dq[3], dk[3];
+  double dense_computed = N * N;
+  if (na::choose_tiles(dg, head_dim, family(dtype), dq, dk))
+    dense_computed = (double)na::count_tiles(dg, dq, dk).computed_slots;
+  r->speedup_bound = c.computed_slots ? dense_computed / (double)c.computed_slots : 0.0;
+  r->perfectly_block_sparse = c.nnz == c.n_full ? 1 : 0;
+  r->form = forward_mode(dtype, head_dim, true);
+  r->cost = cost;
+  r->predicted_kernel_ms = na::predict_kernel_ms(g, batch, heads, head_dim, family(dtype), tq, tkv, c);
+  // permutation passes at the measured ~5 TB/s (bytes read + written) plus
+  // ~8 us per launch
+  int64_t npq = 1, npk = 1;
+  for (int d = 0; d < 3; ++d) {
+    npq *= (int64_t)na::ceil_div(g.L[d], tq[d]) * tq[d];
+    npk *= (int64_t)na::ceil_div(g.L[d], tkv[d]) * tkv[d];
+  }
+  const double bh = (double)batch * heads, eb = elem_bytes(dtype), ob = out_bytes(dtype);
+  double bytes = 2.0 * bh * (N + (double)npk) * head_dim * eb;   // k and v
+  if (r->form == 0)
+    bytes += bh * (N + (double)npq) * head_dim * eb + bh * (N + (double)npq) * (head_dim * ob + 4.0);
+  const int launches = r->form == 0 ? 5 : 2;
+  r->predicted_forward_ms = r->predicted_kernel_ms + bytes / 5.0e12 * 1e3 + launches * 0.008;
+}
+
+na_status na_simulate(int batch, int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                      na_dtype dtype, const int tile_q[3], const int tile_kv[3], na_sim_result* out) {
+  g_err.clear();
+  if (!out) return fail(NA_ERR_INVALID_ARG, "out must be non-null");
+  if ((tile_q == nullptr) != (tile_kv == nullptr)) return fail(NA_ERR_INVALID_ARG, "pass both tile shapes or neither");
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  na::Geometry g = make_geom(grid, window, stride);
+  int tq[3], tk[3];
+  for (int d = 0; d < 3; ++d) {
+    tq[d] = tile_q ? tile_q[d] : lay.tq[d];
+    tk[d] = tile_kv ? tile_kv[d] : lay.tkv[d];
+  }
+  if (!na::check_tile(tq).empty() || !na::check_tile(tk).empty())
+    return fail(NA_ERR_INVALID_ARG, "tile extents must be powers of two");
+  const na::TileCounts c = na::count_tiles(g, tq, tk);
+  double cost = -1.0;
+  for (const auto& cd : na::tile_candidates(g, head_dim, family(dtype)))
+    if (std::equal(cd.tq, cd.tq + 3, tq) && std::equal(cd.tkv, cd.tkv + 3, tk)) cost = cd.cost;
+  fill_sim(batch, heads, head_dim, g, dtype, tq, tk, c, cost, out);
+  return NA_OK;
+}
+
+int na_tile_candidates(int batch, int heads, int head_dim, const int grid[3], const int window[3],
+                       const int stride[3], na_dtype dtype, na_sim_result* out, int capacity) {
+  g_err.clear();
+  if (capacity < 0 || (capacity > 0 && !out)) return fail(NA_ERR_INVALID_ARG, "out must hold capacity entries");
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  na::Geometry g = make_geom(grid, window, stride);
+  const auto cs = na::tile_candidates(g, head_dim, family(dtype));
+  for (int i = 0; i < (int)cs.size() && i < capacity; ++i)
+    fill_sim(batch, heads, head_dim, g, dtype, cs[i].tq, cs[i].tkv, cs[i].c, cs[i].cost, &out[i]);
+  return (int)cs.size();
+}
+
 na_status na_build_tile_map(const int grid[3], const int window[3], const int stride[3], const int tile_q[3],
                             const int tile_kv[3], int32_t* qptr, int32_t* kv_idx, int32_t* n_full,
                             int64_t kv_capacity, int64_t* nnz_out, na_tilemap_stats* stats) {

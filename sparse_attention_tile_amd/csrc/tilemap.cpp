@@ -2,6 +2,7 @@
 #include "tilemap.hpp"
 
 #include <algorithm>
+#include <cmath>
 #include <array>
 #include <limits>
 
@@ -159,56 +160,123 @@ void shapes_with_product(const Geometry& g, int tokens, std::vector<std::array<i
 
 // Relative cost of a (tile_q, tile_kv) pair: computed slots, with a penalty
 // for masked tiles and for the less efficient kernel shapes.
-double tile_cost(const Geometry& g, const int tq[3], const int tkv[3], double q_pen, double kv_pen) {
-  TileCounts c = count_tiles(g, tq, tkv);
+double tile_cost(const TileCounts& c, double q_pen, double kv_pen) {
   const double bfrac = c.nnz ? (double)(c.nnz - c.n_full) / (double)c.nnz : 0.0;
   return (double)c.computed_slots * (1.0 + 0.35 * bfrac) * q_pen * kv_pen;
 }
 
-}  // namespace
+struct Opt { int tok; double pen; };
 
-bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tkv[3]) {
-  struct Opt { int qtok; double qpen; };
-  struct KOpt { int ktok; double kpen; };
-  std::vector<Opt> qopts;
-  std::vector<KOpt> kopts;
-  int min_kv_w = 1;
+// Tile token counts a family's kernels take, with their relative per-slot
+// cost (measured: the 128-query bf16 kernel is 1.3x slower per slot than the
+// 256-query one, 64-key tiles 1.06x slower than 128-key ones).
+bool family_options(Family fam, int head_dim, std::vector<Opt>& qopts, std::vector<Opt>& kopts, int& min_kv_w) {
+  min_kv_w = 1;
   switch (fam) {
     case Family::F32:
       if (head_dim != 32 && head_dim != 64 && head_dim != 128) return false;
       qopts = {{64, 1.0}};
       kopts = {{64, 1.0}};
-      break;
+      return true;
     case Family::MFMA16:
     case Family::FP8:
       if (head_dim != 64 && head_dim != 128) return false;
       qopts = {{256, 1.0}, {128, 1.3}};
       kopts = {{128, 1.0}, {64, 1.06}};
       min_kv_w = 8;   // the boundary mask works on 8-key groups along W
-      break;
+      return true;
   }
-  double best = std::numeric_limits<double>::infinity();
-  bool found = false;
+  return false;
+}
+
+double shape_penalty(Family fam, int qtok, int ktok) {
+  std::vector<Opt> qo, ko;
+  int mw;
+  if (!family_options(fam, 128, qo, ko, mw)) return 1.0;
+  double p = 1.0;
+  for (const auto& o : qo) if (o.tok == qtok) p *= o.pen;
+  for (const auto& o : ko) if (o.tok == ktok) p *= o.pen;
+  return p;
+}
+
+}  // namespace
+
+std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam) {
+  std::vector<Opt> qopts, kopts;
+  int min_kv_w = 1;
+  std::vector<Candidate> out;
+  if (!family_options(fam, head_dim, qopts, kopts, min_kv_w)) return out;
   for (const auto& qo : qopts) {
     std::vector<std::array<int, 3>> qs;
-    shapes_with_product(g, qo.qtok, qs, 1);
+    shapes_with_product(g, qo.tok, qs, 1);
     for (const auto& ko : kopts) {
       std::vector<std::array<int, 3>> ks;
-      shapes_with_product(g, ko.ktok, ks, min_kv_w);
+      shapes_with_product(g, ko.tok, ks, min_kv_w);
       for (const auto& a : qs)
         for (const auto& b : ks) {
-          const int q3[3] = {a[0], a[1], a[2]};
-          const int k3[3] = {b[0], b[1], b[2]};
-          const double cost = tile_cost(g, q3, k3, qo.qpen, ko.kpen);
-          if (cost < best) {
-            best = cost;
-            found = true;
-            for (int d = 0; d < 3; ++d) { tq[d] = a[d]; tkv[d] = b[d]; }
-          }
+          Candidate cd;
+          for (int d = 0; d < 3; ++d) { cd.tq[d] = a[d]; cd.tkv[d] = b[d]; }
+          cd.c = count_tiles(g, cd.tq, cd.tkv);
+          cd.cost = tile_cost(cd.c, qo.pen, ko.pen);
+          out.push_back(cd);
         }
     }
   }
-  return found;
+  // stable: among equal costs the enumeration order (larger Q tiles, larger
+  // KV tiles, T-major shapes first) decides
+  std::stable_sort(out.begin(), out.end(), [](const Candidate& x, const Candidate& y) { return x.cost < y.cost; });
+  return out;
+}
+
+bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tkv[3]) {
+  const std::vector<Candidate> cs = tile_candidates(g, head_dim, fam);
+  if (cs.empty()) return false;
+  for (int d = 0; d < 3; ++d) { tq[d] = cs[0].tq[d]; tkv[d] = cs[0].tkv[d]; }
+  return true;
+}
+
+// Time model.  The kernel runs one workgroup per (batch, head, Q tile); a CU
+// holds up to `slots` of them at once (8-wave workgroups: 1, 4-wave: 2,
+// 1-wave fp32: 8) and runs each one's KV-tile visits back to back.  A visit
+// costs the tile's computed FLOPs (4 x Q slots x KV slots x D) at the family's
+// measured per-CU rate, times the shape penalty, times (1 + kBoundary) when it
+// is a boundary tile; `conc` resident workgroups share the CU, and a
+// workgroup of w waves gets at most w / 8 of it.  Workgroups are dealt in
+// rounds of 256 x slots; the time is rounds x one workgroup's average time,
+// plus a launch overhead.  Calibration (one MI355X, kernel ms measured with
+// HIP events):
+//   bf16 D 128: 1.11e15 FLOP/s on full tiles (91 %-sparse video, 14.1 ms);
+//   boundary tiles 1.2x (video sliding window, 23.5 % boundary, 77.7 ms);
+//   fp8 D 128: 1.46e15 (4K image, 2.26 ms); launch 15 us (64x64 image, 43 us);
+//   fp32: 4.3e13 (16x16 image); bf16 D 64: 0.90e15 (the video block problem
+//   at head_dim 64, 8.66 ms).
+double family_rate(Family fam, int head_dim) {
+  switch (fam) {
+    case Family::MFMA16: return head_dim == 128 ? 1.11e15 : 0.90e15;
+    case Family::FP8: return 1.46e15;
+    case Family::F32: return 4.3e13;
+  }
+  return 1e15;
+}
+
+double predict_kernel_ms(const Geometry& g, int batch, int heads, int head_dim, Family fam, const int tq[3],
+                         const int tkv[3], const TileCounts& c) {
+  constexpr double kLaunchMs = 0.015, kBoundary = 0.2;
+  constexpr int kCUs = 256;
+  (void)g;
+  const int qtok = tq[0] * tq[1] * tq[2], ktok = tkv[0] * tkv[1] * tkv[2];
+  const int waves = fam == Family::F32 ? 1 : std::max(1, qtok / 32);
+  const int slots = std::max(1, 8 / waves);
+  const double n_wg = (double)batch * heads * (double)c.n_q_tiles;
+  if (n_wg <= 0 || c.n_q_tiles == 0) return 0.0;
+  const double conc = std::min((double)slots, std::ceil(n_wg / kCUs));
+  const double per_cu_rate = family_rate(fam, head_dim) / kCUs;
+  const double wg_rate = per_cu_rate * std::min(1.0, conc * waves / 8.0) / conc;
+  const double tile_flop = 4.0 * qtok * ktok * head_dim * shape_penalty(fam, qtok, ktok);
+  const double nb = (double)(c.nnz - c.n_full);
+  const double wg_s = ((double)c.n_full + nb * (1.0 + kBoundary)) / (double)c.n_q_tiles * tile_flop / wg_rate;
+  const double rounds = std::ceil(n_wg / (kCUs * (double)slots));
+  return kLaunchMs + rounds * wg_s * 1e3;
 }
 
 }  // namespace na

@@ -77,4 +77,20 @@ enum class Family { F32, MFMA16, FP8 };
 // head_dim.
 bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tkv[3]);
 
+// One tile-shape candidate of a family, with its counts and relative cost.
+struct Candidate {
+  int tq[3], tkv[3];
+  TileCounts c;
+  double cost;
+};
+
+// Every candidate the chooser considers, sorted by cost (the first one is
+// what choose_tiles returns).  Empty if the family has no kernel for head_dim.
+std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam);
+
+// Predicted attention-kernel time (ms) on one MI355X: a per-CU serial model
+// calibrated on the measured kernels (see the constants in tilemap.cpp).
+double predict_kernel_ms(const Geometry& g, int batch, int heads, int head_dim, Family fam, const int tq[3],
+                         const int tkv[3], const TileCounts& c);
+
 }  // namespace na
