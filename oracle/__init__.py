@@ -1,4 +1,4 @@
-"""CPU oracle for the GNA sparse-attention forward pass.
+"""CPU oracle for the GNA sparse-attention forward and backward passes.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only the test-suite, the smoke check in
@@ -19,6 +19,10 @@ definition states):
   connections without an L x L matrix; softmax kept in FP32 or wider,
   "Sparse attention in video and image generation: optimisation practice",
   section 3.1).
+* ``attend_backward`` -- the gradients of ``attend`` for the loss
+  sum <dout, out> (plain derivatives; GNA page section 5 names training as
+  the next step), with ``query_index_lists`` for the queries that attend a
+  key.
 * ``tile_map`` -- for each query tile, the key tiles it needs, split into
   full and boundary tiles (GNA page, section 1.1 multi-dimensional tiling
   and the perfectly block-sparse case; section 2.1 fine-grained mask only on
@@ -38,3 +42,4 @@ from .gna import (  # noqa: F401
     effective_flops,
     sparsity,
 )
+from .backward import attend_backward, query_index_lists  # noqa: F401

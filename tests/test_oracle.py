@@ -330,3 +330,91 @@ def test_tile_map_stats_regression():
     for g, w, s, tq, tk, nnz, nfull in cases:
         st = oracle.tile_map_stats(g, w, s, tq, tk)
         assert (st["nnz"], st["n_full"]) == (nnz, nfull), g
+
+
+# ----------------------------------------------------------------------------
+# backward oracle pins
+# ----------------------------------------------------------------------------
+
+def _loss(q, k, v, dout, grid, window, stride, scale):
+    out, _ = oracle.attend(q, k, v, grid, window, stride, scale)
+    return float((out * dout).sum())
+
+
+@pytest.mark.parametrize("grid,window,stride", [((1, 4, 5), (1, 3, 2), (1, 1, 2)), ((2, 3, 4), (2, 2, 3), (1, 2, 3))])
+def test_backward_matches_finite_differences(grid, window, stride):
+    # pins the backward to the forward oracle: central differences of
+    # L = sum <dout, attend(q, k, v)> in float64
+    rng = np.random.default_rng(61)
+    N, D, h = math.prod(grid), 3, 2
+    q, k, v, do = (rng.standard_normal((1, N, h, D)) for _ in range(4))
+    scale = 0.7
+    dq, dk, dv = oracle.attend_backward(q, k, v, do, grid, window, stride, scale)
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            x0 = x[idx]
+            x[idx] = x0 + eps
+            lp = _loss(q, k, v, do, grid, window, stride, scale)
+            x[idx] = x0 - eps
+            lm = _loss(q, k, v, do, grid, window, stride, scale)
+            x[idx] = x0
+            num[idx] = (lp - lm) / (2 * eps)
+        assert np.abs(num - g).max() < 1e-7 * max(1.0, np.abs(num).max())
+
+
+def test_backward_dense_limit_matches_autograd():
+    # window = grid: plain softmax attention; torch autograd in float64
+    grid, window, stride = (1, 4, 6), (1, 4, 6), (1, 1, 1)
+    rng = np.random.default_rng(62)
+    N, D, h = 24, 8, 2
+    q, k, v, do = (rng.standard_normal((2, N, h, D)) for _ in range(4))
+    scale = 0.35
+    dq, dk, dv = oracle.attend_backward(q, k, v, do, grid, window, stride, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = torch.einsum("bqhd,bkhd->bhqk", tq, tk) * scale
+    out = torch.einsum("bhqk,bkhd->bqhd", torch.softmax(s, dim=-1), tv)
+    (out * torch.tensor(do)).sum().backward()
+    for a, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.abs(a - t.grad.numpy()).max() < 1e-12
+
+
+def test_backward_window_one():
+    # each query sees only itself: out = v, so dq = dk = 0 and dv = dout
+    grid = (2, 3, 5)
+    rng = np.random.default_rng(63)
+    q, k, v, do = (rng.standard_normal((1, 30, 2, 4)) for _ in range(4))
+    dq, dk, dv = oracle.attend_backward(q, k, v, do, grid, (1, 1, 1), (1, 1, 1), 0.5)
+    # p = exp(s - lse) = 1 up to the rounding of s computed twice
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    assert np.abs(dv - do).max() < 1e-14
+
+
+@pytest.mark.parametrize("grid,window,stride", [((3, 7, 9), (2, 3, 5), (1, 2, 3)), ((1, 12, 12), (1, 5, 5), (1, 1, 1))])
+def test_backward_sum_identities(grid, window, stride):
+    # sum_j dS_ij = 0 for every query, so the dk rows sum to zero; the rows of
+    # p sum to one, so the dv rows sum to the dout rows
+    rng = np.random.default_rng(64)
+    N = math.prod(grid)
+    q, k, v, do = (rng.standard_normal((1, N, 2, 6)) for _ in range(4))
+    dq, dk, dv = oracle.attend_backward(q, k, v, do, grid, window, stride, 0.4)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-11
+    assert np.abs(dv.sum(axis=1) - do.sum(axis=1)).max() < 1e-11
+
+
+def test_backward_selected_rows_match_full():
+    grid, window, stride = (2, 6, 7), (2, 3, 4), (1, 2, 2)
+    rng = np.random.default_rng(65)
+    N = math.prod(grid)
+    q, k, v, do = (rng.standard_normal((2, N, 1, 5)) for _ in range(4))
+    full = oracle.attend_backward(q, k, v, do, grid, window, stride, 0.6)
+    qs, ks = np.array([0, 5, 41, 83]), np.array([3, 17, 60])
+    sel = oracle.attend_backward(q, k, v, do, grid, window, stride, 0.6, queries=qs, keys=ks)
+    assert np.abs(sel[0] - full[0][:, qs]).max() < 1e-13
+    assert np.abs(sel[1] - full[1][:, ks]).max() < 1e-13
+    assert np.abs(sel[2] - full[2][:, ks]).max() < 1e-13
+    # the inverse table is the transpose of the key table
+    ktab = oracle.key_index_table(grid, window, stride)
+    for key, ql in zip(range(N), oracle.query_index_lists(grid, window, stride, np.arange(N))):
+        assert np.array_equal(ql, np.nonzero((ktab == key).any(axis=1))[0])
