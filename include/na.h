@@ -305,6 +305,44 @@ na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt,
                              const int tile_kv[3], float scale, na_dtype dtype,
                              void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Backward pass (bf16).                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of device workspace na_backward needs: tile-ordered copies of q, k,
+ * v and dout plus two fp32 rows per query (linear in N).  0 if the problem
+ * is invalid or unsupported (na_last_error() says why) or empty. */
+size_t na_backward_workspace_bytes(int batch, int heads, int head_dim,
+                                   const int grid[3], const int window[3],
+                                   const int stride[3], na_dtype dtype);
+
+/* Gradients of na_forward (GNA page, section 5: training with the sparse
+ * pattern is the pages' next step; softmax statistics in fp32, SLA page,
+ * section 3.1) for the loss sum <dout, out>, with no gradient through lse:
+ *   p_ij = exp(scale q_i.k_j - lse_i),  D_i = <dout_i, out_i>,
+ *   dS_ij = p_ij (dout_i.v_j - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+ *   dv_j = sum_i p_ij dout_i
+ * over exactly the forward's (query, key) pairs.  bf16 with head_dim 64 or
+ * 128 only (else NA_ERR_UNSUPPORTED); the grid must admit 128-token Q and KV
+ * tiles at least 8 wide along W (W extent >= 5).
+ *
+ * q, k, v  device, the forward's inputs, [batch, T, H, W, heads, head_dim].
+ * out, lse device, the forward's outputs for these inputs (out bf16 as
+ *          na_forward wrote it; lse fp32 [batch, T, H, W, heads]).
+ * dout     device, gradient of the loss with respect to out, same layout.
+ * dq, dk, dv device, bf16, same layout as q; every element is written.
+ * workspace device, caller-owned, >= na_backward_workspace_bytes(...).
+ * Accumulation is fp32; P and dS enter the matrix products as bf16.  No
+ * atomics: each output row is computed by one workgroup, so results are
+ * deterministic.  Other arguments and errors as for na_forward. */
+na_status na_backward(const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, int batch, int heads,
+                      int head_dim, const int grid[3], const int window[3],
+                      const int stride[3], float scale, na_dtype dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ SYMBOLS = (
     "na_choose_tiles", "na_build_tile_map", "na_simulate", "na_tile_candidates", "na_workspace_bytes",
     "na_forward_mode", "na_last_error",
     "na_release_cache", "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
-    "na_attend_kv_tiled",
+    "na_attend_kv_tiled", "na_backward_workspace_bytes", "na_backward",
 )
 
 
@@ -90,6 +90,9 @@ def load():
         "na_attend_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, I3, ctypes.c_float, _i, _fp,
                              _p], _i),
         "na_attend_kv_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, ctypes.c_float, _i, _p], _i),
+        "na_backward_workspace_bytes": ([_i, _i, _i, I3, I3, I3, _i], ctypes.c_size_t),
+        "na_backward": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _p,
+                         ctypes.c_size_t, _p], _i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -216,6 +219,19 @@ def na_attend_kv_tiled(q, kt, vt, out, lse, batch, heads, head_dim, grid, window
                                      _i3(stride), _i3(tile_kv), scale, dtype, stream))
 
 
+def na_backward_workspace_bytes(batch, heads, head_dim, grid, window, stride, dtype) -> int:
+    n = load().na_backward_workspace_bytes(batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride), dtype)
+    if n == 0 and batch > 0 and heads > 0:
+        raise NAError(NA_ERR_INVALID_ARG, na_last_error())
+    return n
+
+
+def na_backward(q, k, v, out, dout, lse, dq, dk, dv, batch, heads, head_dim, grid, window, stride, scale, dtype,
+                workspace, workspace_bytes, stream):
+    _check(load().na_backward(q, k, v, out, dout, lse, dq, dk, dv, batch, heads, head_dim, _i3(grid),
+                              _i3(window), _i3(stride), scale, dtype, workspace, workspace_bytes, stream))
+
+
 # ---------------------------------------------------------------------------
 # torch conveniences (marshalling only)
 # ---------------------------------------------------------------------------
@@ -303,6 +319,30 @@ def forward(q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=Tr
     [B, *grid, heads] fp32 (None if return_lse is False)."""
     f = Forward(q, k, v, window, stride, scale, qkv_scale, return_lse, workspace)
     return f(stream)
+
+
+def backward(q, k, v, out, lse, dout, window, stride=1, scale=None, stream=None):
+    """Gradients (dq, dk, dv) of ``forward`` for the loss sum(dout * out), bf16
+    device tensors in q's layout; ``out`` and ``lse`` are the forward's
+    outputs for the same q, k, v."""
+    torch = _torch()
+    load()
+    for t in (q, k, v, out, dout, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise NAError(NA_ERR_INVALID_ARG, "inputs must be contiguous device tensors")
+    rank = q.dim() - 3
+    grid = grid_of(q)
+    window, stride = _pad3(window, rank), _pad3(stride, rank)
+    B, heads, D = q.shape[0], q.shape[-2], q.shape[-1]
+    dtype = dtype_code(q.dtype)
+    scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    nb = na_backward_workspace_bytes(B, heads, D, grid, window, stride, dtype)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    na_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, heads, D, grid, window, stride, scale, dtype,
+                ws.data_ptr(), nb, _stream_ptr(stream))
+    return dq, dk, dv
 
 
 def permute(x, tile, transpose=False, stream=None):

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libna.so")
 
-SOURCES = ["tilemap.cpp", "na_api.cpp", "permute.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip"]
+SOURCES = ["tilemap.cpp", "na_api.cpp", "permute.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip",
+           "attn_bwd.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.
@@ -38,7 +39,7 @@ def hipcc() -> str:
 # The attention kernels handle no NaN inputs specially and need no IEEE
 # signalling-NaN quieting in min/max: without it fmaxf maps to v_max3_f32
 # with no canonicalising moves.
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"], "attn_bwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 

@@ -47,29 +47,6 @@
 namespace na {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Row of K fed to MFMA row `r` of a 32-key block: quads 1 and 2 of each
-// 16-row group swap places, so that accumulator i of lane half h holds key
-// 16*(i/8) + 8*h + i%8 of the block.
-__device__ __forceinline__ int kperm(int r) { return (((r >> 2) ^ (r >> 3)) & 1) ? (r ^ 12) : r; }
-
-// S^T block kb (32 keys x 32 queries) of the K tile at Ks.
-template <int D, int KROW>
-__device__ __forceinline__ f32x16 qk_block(const unsigned char* Ks, int kb, int krow0, int kswz, int hh,
-                                           const bf16x8* qr) {
-  f32x16 s = f32x16{};
-  const unsigned char* krowp = Ks + (kb * 32 + krow0) * KROW;
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(krowp + (((2 * c + hh) ^ kswz) * 16));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qr[c], s, 0, 0, 0);
-  }
-  return s;
-}
-
 // Lazy rescaling: move the reference max m only when the block max exceeds
 // it by more than thr (= 8 / c2, a factor 2^8 after exp2); then scale l and
 // O by exp2((m_old - m_new) c2).  The branch is wave-uniform and rare.
@@ -112,30 +89,6 @@ __device__ __forceinline__ void tile_to_lds_step_off(const unsigned char* __rest
       __builtin_amdgcn_global_load_lds(base + off[i],
                                        (__attribute__((address_space(3))) void*)(lds + i * ROUND + wv * 1024), 16, 0,
                                        0);
-}
-
-// A operand of O^T = V^T P^T (32 head dims x 16 keys: keys key0 .. key0+15 of
-// the tile, dims 32 db .. 32 db + 31) from a V tile stored [key][d] (rows of
-// 2 D bytes, K's chunk swizzle), with two transposing LDS reads.  Within each
-// group of 16 lanes the read hands lane 4 a + b element b of the 8-byte chunks
-// addressed by lanes a, a + 4, a + 8, a + 12; so lane i of group g addresses
-// key key0 + 8 (g / 2) + 4 r + i / 4 at dims 32 db + 16 (g % 2) + 4 (i % 4),
-// and lane l then holds dim 32 db + l % 32 for keys key0 + 8 (l / 32) + 0..7,
-// the order of the P operand.
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand_tr(const unsigned char* Vs, int key0, int db, int lane) {
-  constexpr int ROWB = D * 2;
-  const int g = lane >> 4, i = lane & 15;
-  const int dcol = 32 * db + 16 * (g & 1) + 4 * (i & 3);          // first of 4 dims
-  const int chunk = (dcol * 2) >> 4, sub = (dcol * 2) & 15;
-  bf16x4 h[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int key = key0 + 8 * (g >> 1) + 4 * r + (i >> 2);
-    const unsigned char* a = Vs + key * ROWB + ((chunk ^ swz<ROWB / 16>(key)) * 16) + sub;
-    h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a);
-  }
-  return bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
 }
 
 template <int D, int NW, int KVT, int IO>

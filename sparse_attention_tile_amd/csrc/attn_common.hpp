@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "kernels.hpp"
@@ -36,6 +37,23 @@ struct KParams {
   int heads;            // heads (grid-order addressing)
 };
 
+// Backward kernels' argument block (see BwdArgs).
+struct BwdParams {
+  KParams kp;
+  const void* dot;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* lse2_t;
+  float* d_t;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* tqptr;
+  const int32_t* tq_idx;
+  const int32_t* tn_full;
+};
+
 inline int host_lg2(int x) {
   int r = 0;
   while ((1 << r) < x) ++r;
@@ -63,7 +81,10 @@ inline KParams make_kparams(const AttnArgs& a) {
   p.nq0 = a.nq[0]; p.nq1 = a.nq[1]; p.nq2 = a.nq[2];
   p.nk1 = a.nk[1]; p.nk2 = a.nk[2];
   p.scale = a.scale;
-  p.c2 = a.scale * 1.4426950408889634f;
+  // scale * log2(e), kept >= 1e-30 so that a masked score (-inf) times c2
+  // stays -inf when scale is 0 (finite scores times 1e-30 still round to 0
+  // in exp2)
+  p.c2 = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   p.v_scale = a.v_scale;
   p.heads = a.heads;
   return p;

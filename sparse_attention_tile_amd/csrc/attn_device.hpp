@@ -117,4 +117,58 @@ __device__ __forceinline__ uint64_t boundary_mask(SlotFn slot0, int k0, int k1, 
   return vmask;
 }
 
+// ---- bf16 MFMA operand helpers shared by the forward and backward kernels
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Row of an LDS tile fed to MFMA row `r` of a 32-row block: quads 1 and 2 of
+// each 16-row group swap places, so that accumulator i of lane half h holds
+// row 16*(i/8) + 8*h + i%8 of the block (two runs of 8 consecutive rows, the
+// k order of a B operand).
+__device__ __forceinline__ int kperm(int r) { return (((r >> 2) ^ (r >> 3)) & 1) ? (r ^ 12) : r; }
+
+// 32 rows (block kb) of an LDS tile of [row][D] bf16 rows times the register
+// operand br (B: D x 32 columns, lane n holds 8 consecutive dims of column n
+// per 16-dim step): a 32 x 32 fp32 block, lane = column, accumulator i = row
+// 16*(i/8) + 8*h + i%8.  With K rows and Q columns this is S^T = K Q^T.
+template <int D, int ROWB>
+__device__ __forceinline__ f32x16 qk_block(const unsigned char* Ts, int kb, int row0, int rswz, int hh,
+                                           const bf16x8* br) {
+  f32x16 s = f32x16{};
+  const unsigned char* rowp = Ts + (kb * 32 + row0) * ROWB;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(rowp + (((2 * c + hh) ^ rswz) * 16));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, br[c], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// A operand of O^T = V^T P^T (32 head dims x 16 keys: keys key0 .. key0+15 of
+// the tile, dims 32 db .. 32 db + 31) from a tile stored [key][d] (rows of
+// 2 D bytes, the chunk swizzle above), with two transposing LDS reads.  Any
+// [row][d] tile works the same way (the backward reads K^T, Q^T, dO^T so).  Within each
+// group of 16 lanes the read hands lane 4 a + b element b of the 8-byte chunks
+// addressed by lanes a, a + 4, a + 8, a + 12; so lane i of group g addresses
+// key key0 + 8 (g / 2) + 4 r + i / 4 at dims 32 db + 16 (g % 2) + 4 (i % 4),
+// and lane l then holds dim 32 db + l % 32 for keys key0 + 8 (l / 32) + 0..7,
+// the order of the P operand.
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand_tr(const unsigned char* Vs, int key0, int db, int lane) {
+  constexpr int ROWB = D * 2;
+  const int g = lane >> 4, i = lane & 15;
+  const int dcol = 32 * db + 16 * (g & 1) + 4 * (i & 3);          // first of 4 dims
+  const int chunk = (dcol * 2) >> 4, sub = (dcol * 2) & 15;
+  bf16x4 h[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int key = key0 + 8 * (g >> 1) + 4 * r + (i >> 2);
+    const unsigned char* a = Vs + key * ROWB + ((chunk ^ swz<ROWB / 16>(key)) * 16) + sub;
+    h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)a);
+  }
+  return bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+}
+
 }  // namespace na

@@ -43,6 +43,30 @@ bool attn_bf16_tile_ok(const int tile_kv[3]);
 // Whether the bf16 kernel can read and write grid order directly.
 bool attn_bf16_grid_io_supported(int head_dim);
 
+// Backward pass (bf16): the forward's problem description plus the extra
+// tensors.  attn.qt/kt/vt hold q, k, v in tile order (plain rows); dot holds
+// dO in tile order; out, dout, lse are the caller's grid-order tensors;
+// lse2_t and d_t are tile-order fp32 scratch the prep kernel fills; dq, dk,
+// dv are written in grid order; tqptr/tq_idx/tn_full are the transposed tile
+// map (per KV tile, its Q tiles, full ones first).
+struct BwdArgs {
+  AttnArgs attn;
+  const void* dot;
+  const void* out;
+  const void* dout;
+  const float* lse;
+  float* lse2_t;
+  float* d_t;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* tqptr;
+  const int32_t* tq_idx;
+  const int32_t* tn_full;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+bool attn_bwd_supported(int head_dim, int q_tokens, int kv_tokens);
+
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
 size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);
 

@@ -80,10 +80,14 @@ struct Plan {
   int32_t* d_qptr = nullptr;
   int32_t* d_kv = nullptr;
   int32_t* d_nfull = nullptr;
+  // transposed map (built the first time the backward needs it)
+  bool has_t = false;
+  int32_t* d_tptr = nullptr;
+  int32_t* d_tidx = nullptr;
+  int32_t* d_tnfull = nullptr;
   ~Plan() {
-    if (d_qptr) (void)hipFree(d_qptr);
-    if (d_kv) (void)hipFree(d_kv);
-    if (d_nfull) (void)hipFree(d_nfull);
+    for (int32_t* q : {d_qptr, d_kv, d_nfull, d_tptr, d_tidx, d_tnfull})
+      if (q) (void)hipFree(q);
   }
 };
 
@@ -127,6 +131,29 @@ na_status get_plan(const na::Geometry& g, const int tq[3], const int tkv[3], Pla
     return fail(NA_ERR_HIP, "upload of the device tile map failed");
   *out = p.get();
   plans()[key] = std::move(p);
+  return NA_OK;
+}
+
+// The plan plus its transposed map on the device.
+na_status get_plan_t(const na::Geometry& g, const int tq[3], const int tkv[3], Plan** out) {
+  Plan* p = nullptr;
+  na_status st = get_plan(g, tq, tkv, &p);
+  if (st != NA_OK) return st;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!p->has_t) {
+    const na::TransposedMap t = na::transpose_tile_map(p->map);
+    const size_t nk = t.n_full.size(), nnz = t.q_idx.size();
+    if (hipMalloc(&p->d_tptr, (nk + 1) * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(&p->d_tidx, (nnz ? nnz : 1) * sizeof(int32_t)) != hipSuccess ||
+        hipMalloc(&p->d_tnfull, (nk ? nk : 1) * sizeof(int32_t)) != hipSuccess)
+      return fail(NA_ERR_HIP, "hipMalloc of the transposed tile map failed");
+    if (hipMemcpy(p->d_tptr, t.kptr.data(), (nk + 1) * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess ||
+        (nnz && hipMemcpy(p->d_tidx, t.q_idx.data(), nnz * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) ||
+        (nk && hipMemcpy(p->d_tnfull, t.n_full.data(), nk * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess))
+      return fail(NA_ERR_HIP, "upload of the transposed tile map failed");
+    p->has_t = true;
+  }
+  *out = p;
   return NA_OK;
 }
 
@@ -431,20 +458,10 @@ na_status na_unpermute_lse(const float* lse_t, float* lse, int batch, int heads,
                     "lse unpermute launch");
 }
 
-static na_status attend_impl(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
-                             int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
-                             const Layout& lay, float scale, na_dtype dtype, const float* qkv_scale,
-                             int io_mode, hipStream_t stream) {
-  na::Geometry g = make_geom(grid, window, stride);
-  Plan* plan = nullptr;
-  na_status st = get_plan(g, lay.tq, lay.tkv, &plan);
-  if (st != NA_OK) return st;
-  na::AttnArgs a;
-  a.qt = qt;
-  a.kt = kt;
-  a.vt = vt;
-  a.ot = ot;
-  a.lse_t = lse_t;
+// Kernel arguments of one problem: geometry, tiles and the plan's map.
+static na::AttnArgs attn_args(const na::Geometry& g, const Plan* plan, const int tq[3], const int tkv[3],
+                              int batch, int heads, int head_dim, float scale) {
+  na::AttnArgs a{};
   a.qptr = plan->d_qptr;
   a.kv_idx = plan->d_kv;
   a.n_full = plan->d_nfull;
@@ -455,13 +472,30 @@ static na_status attend_impl(const void* qt, const void* kt, const void* vt, voi
     a.L[d] = g.L[d];
     a.w[d] = g.w[d];
     a.s[d] = g.s[d];
-    a.tq[d] = lay.tq[d];
-    a.tkv[d] = lay.tkv[d];
-    a.nq[d] = lay.nq[d];
-    a.nk[d] = lay.nk[d];
+    a.tq[d] = tq[d];
+    a.tkv[d] = tkv[d];
+    a.nq[d] = na::ceil_div(g.L[d], tq[d]);
+    a.nk[d] = na::ceil_div(g.L[d], tkv[d]);
   }
   a.scale = scale;
   a.v_scale = 1.0f;
+  return a;
+}
+
+static na_status attend_impl(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
+                             int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                             const Layout& lay, float scale, na_dtype dtype, const float* qkv_scale,
+                             int io_mode, hipStream_t stream) {
+  na::Geometry g = make_geom(grid, window, stride);
+  Plan* plan = nullptr;
+  na_status st = get_plan(g, lay.tq, lay.tkv, &plan);
+  if (st != NA_OK) return st;
+  na::AttnArgs a = attn_args(g, plan, lay.tq, lay.tkv, batch, heads, head_dim, scale);
+  a.qt = qt;
+  a.kt = kt;
+  a.vt = vt;
+  a.ot = ot;
+  a.lse_t = lse_t;
   a.io_mode = io_mode;
   if (dtype == NA_FP8_E4M3 && qkv_scale) {
     a.scale = scale * qkv_scale[0] * qkv_scale[1];
@@ -605,6 +639,125 @@ na_status na_forward(const void* q, const void* k, const void* v, void* out, flo
       return st;
   }
   return NA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// backward
+
+namespace {
+
+// Tile shapes and tile-order buffers of one backward problem.
+struct BwdLayout {
+  int tq[3], tkv[3];
+  size_t q_bytes, kv_bytes, stat_bytes;
+  size_t off_q, off_k, off_v, off_do, off_l, off_d, total;
+};
+
+na_status check_bwd(int batch, int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                    na_dtype dtype, BwdLayout* b) {
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (dtype != NA_BF16 || (head_dim != 64 && head_dim != 128))
+    return fail(NA_ERR_UNSUPPORTED, "the backward is built for bf16 with head_dim 64 or 128");
+  // 128-query and 128-key tiles, both at least 8 wide along W: the cheapest
+  // such pair of the forward's candidates
+  const na::Geometry g = make_geom(grid, window, stride);
+  bool found = false;
+  for (const auto& c : na::tile_candidates(g, head_dim, na::Family::MFMA16)) {
+    if (c.tq[0] * c.tq[1] * c.tq[2] != 128 || c.tkv[0] * c.tkv[1] * c.tkv[2] != 128 || c.tq[2] < 8 ||
+        c.tkv[2] < 8)
+      continue;
+    for (int d = 0; d < 3; ++d) {
+      b->tq[d] = c.tq[d];
+      b->tkv[d] = c.tkv[d];
+    }
+    found = true;
+    break;
+  }
+  if (!found) return fail(NA_ERR_UNSUPPORTED, "no 128 x 128 tile pair at least 8 wide along W fits this grid");
+  int64_t npq = 1, npk = 1;
+  for (int d = 0; d < 3; ++d) {
+    npq *= (int64_t)na::ceil_div(grid[d], b->tq[d]) * b->tq[d];
+    npk *= (int64_t)na::ceil_div(grid[d], b->tkv[d]) * b->tkv[d];
+  }
+  const size_t bh = (size_t)batch * heads;
+  b->q_bytes = bh * npq * head_dim * 2;
+  b->kv_bytes = bh * npk * head_dim * 2;
+  b->stat_bytes = bh * npq * sizeof(float);
+  b->off_q = 0;
+  b->off_k = b->off_q + round256(b->q_bytes);
+  b->off_v = b->off_k + round256(b->kv_bytes);
+  b->off_do = b->off_v + round256(b->kv_bytes);
+  b->off_l = b->off_do + round256(b->q_bytes);
+  b->off_d = b->off_l + round256(b->stat_bytes);
+  b->total = b->off_d + round256(b->stat_bytes);
+  return NA_OK;
+}
+
+}  // namespace
+
+size_t na_backward_workspace_bytes(int batch, int heads, int head_dim, const int grid[3], const int window[3],
+                                   const int stride[3], na_dtype dtype) {
+  g_err.clear();
+  BwdLayout b;
+  if (check_bwd(batch, heads, head_dim, grid, window, stride, dtype, &b) != NA_OK) return 0;
+  return b.total;
+}
+
+na_status na_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                      const float* lse, void* dq, void* dk, void* dv, int batch, int heads, int head_dim,
+                      const int grid[3], const int window[3], const int stride[3], float scale, na_dtype dtype,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  BwdLayout b;
+  na_status st = check_bwd(batch, heads, head_dim, grid, window, stride, dtype, &b);
+  if (st != NA_OK) return st;
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv)
+    return fail(NA_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk and dv must be non-null");
+  for (const void* x : {q, k, v, out, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(x)) return fail(NA_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(lse) & 3u) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  st = check_scales(scale, dtype, nullptr);
+  if (st != NA_OK) return st;
+  if (!workspace) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null");
+  if (!aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < b.total)
+    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(b.total) + " bytes");
+  const na::Geometry g = make_geom(grid, window, stride);
+  Plan* plan = nullptr;
+  st = get_plan_t(g, b.tq, b.tkv, &plan);
+  if (st != NA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  void* qt = ws + b.off_q;
+  void* kt = ws + b.off_k;
+  void* vt = ws + b.off_v;
+  void* dot = ws + b.off_do;
+  if ((st = hip_status(na::launch_permute(q, qt, batch, heads, head_dim, grid, b.tq, 2, 0, s), "permute q")) ||
+      (st = hip_status(na::launch_permute(k, kt, batch, heads, head_dim, grid, b.tkv, 2, 0, s), "permute k")) ||
+      (st = hip_status(na::launch_permute(v, vt, batch, heads, head_dim, grid, b.tkv, 2, 0, s), "permute v")) ||
+      (st = hip_status(na::launch_permute(dout, dot, batch, heads, head_dim, grid, b.tq, 2, 0, s), "permute dout")))
+    return st;
+  na::BwdArgs a{};
+  a.attn = attn_args(g, plan, b.tq, b.tkv, batch, heads, head_dim, scale);
+  a.attn.qt = qt;
+  a.attn.kt = kt;
+  a.attn.vt = vt;
+  a.dot = dot;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.lse2_t = reinterpret_cast<float*>(ws + b.off_l);
+  a.d_t = reinterpret_cast<float*>(ws + b.off_d);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.tqptr = plan->d_tptr;
+  a.tq_idx = plan->d_tidx;
+  a.tn_full = plan->d_tnfull;
+  return hip_status(na::launch_bwd(a, s), "backward launch");
 }
 
 }  // extern "C"

@@ -133,6 +133,35 @@ TileMap build_tile_map(const Geometry& g, const int tq[3], const int tkv[3]) {
   return m;
 }
 
+TransposedMap transpose_tile_map(const TileMap& m) {
+  TransposedMap t;
+  const int64_t nK = (int64_t)m.nk[0] * m.nk[1] * m.nk[2];
+  const int64_t nQ = (int64_t)m.n_full.size();
+  std::vector<int32_t> nf(nK, 0), nb(nK, 0);
+  for (int64_t a = 0; a < nQ; ++a)
+    for (int32_t e = m.qptr[a]; e < m.qptr[a + 1]; ++e) {
+      const bool full = e - m.qptr[a] < m.n_full[a];
+      (full ? nf : nb)[m.kv_idx[e]]++;
+    }
+  t.kptr.assign(nK + 1, 0);
+  for (int64_t c = 0; c < nK; ++c) t.kptr[c + 1] = t.kptr[c] + nf[c] + nb[c];
+  t.n_full = nf;
+  t.q_idx.assign(t.kptr[nK], 0);
+  std::vector<int32_t> fpos(nK), bpos(nK);
+  for (int64_t c = 0; c < nK; ++c) {
+    fpos[c] = t.kptr[c];
+    bpos[c] = t.kptr[c] + nf[c];
+  }
+  // Q tiles visited in ascending order, so each part comes out ascending
+  for (int64_t a = 0; a < nQ; ++a)
+    for (int32_t e = m.qptr[a]; e < m.qptr[a + 1]; ++e) {
+      const int32_t c = m.kv_idx[e];
+      const bool full = e - m.qptr[a] < m.n_full[a];
+      t.q_idx[full ? fpos[c]++ : bpos[c]++] = (int32_t)a;
+    }
+  return t;
+}
+
 namespace {
 
 int pow2_ceil(int x) { int p = 1; while (p < x) p <<= 1; return p; }

@@ -69,6 +69,16 @@ struct TileMap {
 // tiles (ascending), then the boundary tiles (ascending).
 TileMap build_tile_map(const Geometry& g, const int tq[3], const int tkv[3]);
 
+// The transpose of a tile map: for each KV tile (row-major index), the Q
+// tiles whose rows list it -- full ones first, then boundary ones, each
+// ascending (the backward's dK/dV kernel walks these rows).
+struct TransposedMap {
+  std::vector<int32_t> kptr;    // [nK + 1]
+  std::vector<int32_t> q_idx;   // [nnz] row-major linear Q-tile index
+  std::vector<int32_t> n_full;  // [nK]
+};
+TransposedMap transpose_tile_map(const TileMap& m);
+
 // Kernel families the library has (tile token counts they take).
 enum class Family { F32, MFMA16, FP8 };
 

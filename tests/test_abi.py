@@ -180,3 +180,30 @@ def test_last_error_is_per_call(na):
     assert na.na_last_error() != ""
     na.na_choose_tiles((1, 16, 16), (1, 5, 5), (1, 1, 1), 64, na.NA_BF16)
     assert na.na_last_error() == ""
+
+
+def test_backward_arguments_rejected(na):
+    lib = na.load()
+    I3 = na.I3
+    g, w, s = I3(1, 16, 16), I3(1, 5, 5), I3(1, 1, 1)
+    fake = 1 << 20
+    ws = na.na_backward_workspace_bytes(1, 1, 64, (1, 16, 16), (1, 5, 5), (1, 1, 1), na.NA_BF16)
+    assert ws > 0
+
+    def bwd(dt=na.NA_BF16, D=64, ws_bytes=ws, lse=fake, grid=g, ws_ptr=fake):
+        return lib.na_backward(fake, fake, fake, fake, fake, lse, fake, fake, fake, 1, 1, D, grid, w, s, 0.125,
+                               dt, ws_ptr, ws_bytes, None)
+
+    assert bwd(dt=na.NA_F32) == na.NA_ERR_UNSUPPORTED
+    assert bwd(dt=na.NA_FP8_E4M3) == na.NA_ERR_UNSUPPORTED
+    assert bwd(D=48) == na.NA_ERR_UNSUPPORTED
+    assert bwd(grid=I3(1, 16, 3)) != na.NA_OK          # window 5 > W 3: invalid geometry
+    assert bwd(lse=None) == na.NA_ERR_INVALID_ARG
+    assert bwd(ws_ptr=None) == na.NA_ERR_INVALID_ARG
+    assert bwd(ws_bytes=ws - 1) == na.NA_ERR_WORKSPACE
+    # W extent 4 cannot hold an 8-wide tile
+    assert lib.na_backward_workspace_bytes(1, 1, 64, I3(1, 64, 4), I3(1, 5, 3), I3(1, 1, 1), na.NA_BF16) == 0
+    # linear in the token count
+    a = na.na_backward_workspace_bytes(1, 2, 128, (1, 64, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
+    b = na.na_backward_workspace_bytes(1, 2, 128, (1, 128, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
+    assert 1.9 < b / a < 2.1
