@@ -123,6 +123,7 @@ def main():
                     help="run the workload's geometry at another head_dim (synthetic inputs of that shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -269,6 +270,33 @@ def main():
             "kernel_source_sha256_16": src_hash,
         },
     }
+
+    # backward pass (bf16): gradients for a seeded dout, timed like the stages
+    if not args.no_backward and dcode == na.NA_BF16 and D in (64, 128):
+        try:
+            nbw = na.na_backward_workspace_bytes(B, H, D, wl.grid, wl.window, wl.stride, dcode)
+        except na.NAError:
+            nbw = 0
+        if nbw:
+            g = torch.Generator("cpu").manual_seed(wl.seed + 3)
+            dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+            fwd()
+            ws_b = torch.empty(nbw, dtype=torch.uint8, device="cuda")
+            grads = [torch.empty_like(q) for _ in range(3)]
+
+            def bwd():
+                na.na_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), fwd.out.data_ptr(), dout.data_ptr(),
+                               fwd.lse.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+                               B, H, D, wl.grid, wl.window, wl.stride, wl.scale, dcode, ws_b.data_ptr(), nbw, stream)
+
+            b_ms = stage_ms(bwd)
+            result["backward"] = {
+                "ms": b_ms,
+                "effective_TFLOPs": 2.5 * eff / (b_ms * 1e-3) / 1e12,
+                "flops": "2.5 x the forward's effective FLOPs (S, dP, dV, dK, dQ products); the kernels compute "
+                         "7 products per pair (S and dP in both the dq and the dk/dv kernel)",
+            }
+            del ws_b, grads, dout
 
     # the analytic model's prediction for the same problem, beside the measurement
     sim = na.na_simulate(B, H, D, wl.grid, wl.window, wl.stride, dcode)

@@ -89,6 +89,25 @@ def test_zero_queries_give_window_mean(na, path):
     assert float((lse.cpu().double() - math.log(math.prod(wl.window))).abs().max()) <= 1e-5
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_zero_scale_gives_window_mean(na, dtype, path):
+    # scale 0: every weight is 1, so out is the window mean of v and
+    # lse = ln prod(w) exactly as for q = 0; boundary tiles (masked keys)
+    # must not turn 0 * -inf into NaN
+    base = WORKLOADS["img64_block"] if dtype == "bf16" else WORKLOADS["img256_block_fp8"]
+    wl = base.with_(grid=(2, 21, 18), window=(2, 6, 5), stride=(1, 3, 2), heads=2, seed=95, head_dim=128)
+    say(f"[special] scale = 0 ({dtype})")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=0.0, qkv_scale=sc if dtype == "fp8" else None)
+    out, lse = f()
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    assert float((lse.cpu().double() - math.log(math.prod(wl.window))).abs().max()) <= 1e-5
+    zq = torch.zeros_like(qc)   # the oracle with q = 0 gives the same uniform weights
+    eo, _ = compare(wl, zq, kc, vc, sc, out, lse)
+    assert eo <= TOL[dtype][0]
+
+
 @pytest.mark.parametrize("stride", [(1, 1, 1), (2, 3, 4)])
 def test_window_equal_grid_is_dense(na, stride, path):
     wl = WORKLOADS["img64_block"].with_(grid=(2, 12, 16), window=(2, 12, 16), stride=stride, heads=2,
