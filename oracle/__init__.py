@@ -23,6 +23,9 @@ definition states):
   sum <dout, out> (plain derivatives; GNA page section 5 names training as
   the next step), with ``query_index_lists`` for the queries that attend a
   key.
+* ``topk_select`` / ``topk_attend`` -- content-selected block sparsity:
+  block-mean importance scores, the top-k KV tiles per Q tile, attention
+  over the kept tiles (tutorial section 6; overview page section 2.2).
 * ``tile_map`` -- for each query tile, the key tiles it needs, split into
   full and boundary tiles (GNA page, section 1.1 multi-dimensional tiling
   and the perfectly block-sparse case; section 2.1 fine-grained mask only on
@@ -43,3 +46,11 @@ from .gna import (  # noqa: F401
     sparsity,
 )
 from .backward import attend_backward, query_index_lists  # noqa: F401
+from .topk import (  # noqa: F401
+    block_means_f32,
+    block_scores_f32,
+    kv_tile_is_full,
+    select_blocks,
+    topk_attend,
+    topk_select,
+)

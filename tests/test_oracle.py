@@ -418,3 +418,85 @@ def test_backward_selected_rows_match_full():
     ktab = oracle.key_index_table(grid, window, stride)
     for key, ql in zip(range(N), oracle.query_index_lists(grid, window, stride, np.arange(N))):
         assert np.array_equal(ql, np.nonzero((ktab == key).any(axis=1))[0])
+
+
+# ----------------------------------------------------------------------------
+# content-selected block sparsity (top-k) oracle pins
+# ----------------------------------------------------------------------------
+
+def test_topk_all_blocks_is_dense_attention():
+    # keep = every KV tile: attention over all keys, i.e. plain softmax
+    # attention (torch SDPA in float64)
+    grid, tq, tk = (2, 6, 8), (1, 4, 4), (2, 2, 4)
+    rng = np.random.default_rng(71)
+    N = math.prod(grid)
+    q, k, v = (rng.standard_normal((1, N, 2, 8)).astype(np.float32) for _ in range(3))
+    nK = math.prod(-(-L // t) for L, t in zip(grid, tk))
+    out, lse = oracle.topk_attend(q, k, v, grid, tq, tk, nK, 0.3)
+    ref, rlse = _torch_sdpa64(*(x.astype(np.float64) for x in (q, k, v)), 0.3)
+    assert np.abs(out - ref).max() < 1e-12 and np.abs(lse - rlse).max() < 1e-12
+
+
+def test_topk_scores_against_plain_means():
+    # the float32-order scores equal the plain float64 definition to float32
+    # accuracy, and the selected tiles are the top-k of the float64 scores
+    # whenever the gap at the cut is wide
+    grid, tq, tk = (3, 5, 9), (1, 4, 4), (1, 2, 4)
+    rng = np.random.default_rng(72)
+    N = math.prod(grid)
+    q, k = (rng.standard_normal((1, N, 1, 16)).astype(np.float32) for _ in range(2))
+    qm = oracle.block_means_f32(q, grid, tq)
+    km = oracle.block_means_f32(k, grid, tk)
+    s32 = oracle.block_scores_f32(qm, km)[0, 0]
+
+    def tiles(tile):
+        nt = [-(-L // t) for L, t in zip(grid, tile)]
+        lists = []
+        for a in range(math.prod(nt)):
+            a0, rem = divmod(a, nt[1] * nt[2])
+            a1, a2 = divmod(rem, nt[2])
+            toks = [(t * grid[1] + y) * grid[2] + x
+                    for t in range(a0 * tile[0], min((a0 + 1) * tile[0], grid[0]))
+                    for y in range(a1 * tile[1], min((a1 + 1) * tile[1], grid[1]))
+                    for x in range(a2 * tile[2], min((a2 + 1) * tile[2], grid[2]))]
+            lists.append(toks)
+        return lists
+
+    qmean = np.array([q[0, t, 0].astype(np.float64).mean(axis=0) for t in tiles(tq)])
+    kmean = np.array([k[0, t, 0].astype(np.float64).mean(axis=0) for t in tiles(tk)])
+    s64 = qmean @ kmean.T
+    assert np.abs(s32 - s64).max() < 1e-5 * max(1.0, np.abs(s64).max())
+    keep = 5
+    idx, nf = oracle.topk_select(q, k, grid, tq, tk, keep)
+    for a in range(s64.shape[0]):
+        srt = np.sort(s64[a])[::-1]
+        if srt[keep - 1] - srt[keep] > 1e-4:
+            assert set(idx[0, 0, a]) == set(np.argsort(-s64[a])[:keep])
+
+
+def test_topk_single_dominant_block():
+    # keys of one KV tile align with every query, the rest are orthogonal:
+    # keep = 1 picks that tile and the attention is over its keys only
+    grid, tq, tk = (1, 8, 8), (1, 4, 8), (1, 4, 4)
+    N, D = 64, 4
+    q = np.zeros((1, N, 1, D), dtype=np.float32)
+    k = np.zeros((1, N, 1, D), dtype=np.float32)
+    q[..., 0] = 1.0
+    k[..., 1] = 1.0
+    hot = oracle.topk.__dict__["_tile_tokens"](grid, tk, 3)
+    k[0, hot, 0, 0] = 2.0
+    idx, nf = oracle.topk_select(q, k, grid, tq, tk, 1)
+    assert (idx == 3).all() and (nf == 1).all()
+    rng = np.random.default_rng(73)
+    v = rng.standard_normal((1, N, 1, D))
+    out, lse = oracle.topk_attend(q, k, v, grid, tq, tk, 1, 0.5)
+    assert np.abs(out[0, :, 0] - v[0, hot, 0].mean(axis=0)).max() < 1e-12   # equal scores in the tile
+    assert np.abs(lse - (0.5 * 2.0 + math.log(len(hot)))).max() < 1e-12
+
+
+def test_topk_selection_order_and_ties():
+    scores = np.array([[[3.0, 1.0, 3.0, 2.0, 3.0]]], dtype=np.float32)
+    full = np.array([True, True, False, True, True])
+    idx, nf = oracle.select_blocks(scores, 3, full)
+    # best three: indices 0, 2, 4 (score 3, ties by index); full ones first
+    assert idx.tolist() == [[[0, 4, 2]]] and nf.tolist() == [[2]]
