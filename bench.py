@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-topk", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -297,6 +298,42 @@ def main():
                          "7 products per pair (S and dP in both the dq and the dk/dv kernel)",
             }
             del ws_b, grads, dout
+
+    # content-selected block sparsity at the same density: keep the KV tiles
+    # whose keys match the workload's keys per query
+    if not args.no_topk and dcode == na.NA_BF16 and D in (64, 128):
+        try:
+            ttq, ttk = na.na_topk_tiles(wl.grid, D, dcode)
+        except na.NAError:
+            ttq = None
+        if ttq is not None:
+            nk_t = math.prod(-(-L // t) for L, t in zip(wl.grid, ttk))
+            keep = max(1, min(nk_t, round(wl.keys_per_query / math.prod(ttk))))
+            nbt = na.na_topk_workspace_bytes(B, H, D, wl.grid, keep, dcode)
+            ws_t = torch.empty(nbt, dtype=torch.uint8, device="cuda")
+            nq_t = math.prod(-(-L // t) for L, t in zip(wl.grid, ttq))
+            idx_t = torch.empty((B * H, nq_t, keep), dtype=torch.int32, device="cuda")
+            nf_t = torch.empty((B * H, nq_t), dtype=torch.int32, device="cuda")
+
+            def topk_fwd():
+                na.load().na_topk_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), fwd.out.data_ptr(),
+                                          fwd.lse.data_ptr(), B, H, D, na.I3(*wl.grid), keep, wl.scale, dcode,
+                                          ws_t.data_ptr(), nbt, stream)
+
+            def topk_sel():
+                na.load().na_topk_select(q.data_ptr(), k.data_ptr(), B, H, D, na.I3(*wl.grid), keep, dcode,
+                                         idx_t.data_ptr(), nf_t.data_ptr(), ws_t.data_ptr(), nbt, stream)
+
+            t_ms, s_ms = stage_ms(topk_fwd), stage_ms(topk_sel)
+            # keys attended per query: the real keys of the kept tiles (all tiles full here or close)
+            keys = keep * math.prod(ttk)
+            eff_t = 4.0 * B * H * wl.tokens * keys * D
+            result["topk"] = {
+                "keep": keep, "of_kv_tiles": nk_t, "tile_q": list(ttq), "tile_kv": list(ttk),
+                "ms": t_ms, "select_ms": s_ms, "effective_TFLOPs": eff_t / (t_ms * 1e-3) / 1e12,
+                "effective_flops": eff_t,
+            }
+            del ws_t, idx_t, nf_t
 
     # the analytic model's prediction for the same problem, beside the measurement
     sim = na.na_simulate(B, H, D, wl.grid, wl.window, wl.stride, dcode)

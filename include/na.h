@@ -306,6 +306,49 @@ na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt,
                              void* stream);
 
 /* ---------------------------------------------------------------------- */
+/* Content-selected block sparsity (bf16).                                 */
+/* ---------------------------------------------------------------------- */
+/* The tutorial (section 6) scores blocks by importance, keeps the best ones
+ * and skips the rest whole; the overview page (section 2.2) names top-k
+ * selection.  Here: blocks are the library's tiles of the dense geometry
+ * (na_topk_tiles), score(a, c) = <mean q over the real tokens of Q tile a,
+ * mean k over the real tokens of KV tile c>, and each Q tile keeps its
+ * `keep` best KV tiles (equal scores: lower index first); every query of a
+ * Q tile attends to every real key of its kept tiles.  Scores are evaluated
+ * in float32 in a fixed order (token-by-token sums in in-tile row-major
+ * order, IEEE division by the count, product-by-product sums over the head
+ * dimension, no fused multiply-add), so the selection is reproducible bit
+ * for bit.  bf16, head_dim 64 or 128; 1 <= keep <= number of KV tiles. */
+
+/* Tile (block) shapes top-k selection uses for this grid (host). */
+na_status na_topk_tiles(const int grid[3], int head_dim, na_dtype dtype,
+                        int tile_q[3], int tile_kv[3]);
+
+/* Device workspace bytes of na_topk_select / na_topk_forward (linear in N
+ * plus the B*heads*nQ*keep tile map). 0 if invalid (na_last_error()). */
+size_t na_topk_workspace_bytes(int batch, int heads, int head_dim,
+                               const int grid[3], int keep, na_dtype dtype);
+
+/* The selection alone.  kv_idx: device int32 [batch*heads, nQ, keep], each
+ * row full tiles (no padding slot) first, then the others, each ascending;
+ * n_full: device int32 [batch*heads, nQ].  q, k as for na_forward. */
+na_status na_topk_select(const void* q, const void* k, int batch, int heads,
+                         int head_dim, const int grid[3], int keep,
+                         na_dtype dtype, int32_t* kv_idx, int32_t* n_full,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Selection, then attention over the kept tiles (k and v permuted to tile
+ * order; the bf16 attention kernel reads q and writes out and lse in grid
+ * order, one tile map per (batch, head)).  Tensors and errors as for
+ * na_forward (lse may be NULL). */
+na_status na_topk_forward(const void* q, const void* k, const void* v,
+                          void* out, float* lse, int batch, int heads,
+                          int head_dim, const int grid[3], int keep,
+                          float scale, na_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
 /* Backward pass (bf16).                                                   */
 /* ---------------------------------------------------------------------- */
 

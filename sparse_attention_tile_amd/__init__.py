@@ -25,7 +25,8 @@ SYMBOLS = (
     "na_choose_tiles", "na_build_tile_map", "na_simulate", "na_tile_candidates", "na_workspace_bytes",
     "na_forward_mode", "na_last_error",
     "na_release_cache", "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
-    "na_attend_kv_tiled", "na_backward_workspace_bytes", "na_backward",
+    "na_attend_kv_tiled", "na_backward_workspace_bytes", "na_backward", "na_topk_tiles",
+    "na_topk_workspace_bytes", "na_topk_select", "na_topk_forward",
 )
 
 
@@ -91,6 +92,11 @@ def load():
                              _p], _i),
         "na_attend_kv_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, ctypes.c_float, _i, _p], _i),
         "na_backward_workspace_bytes": ([_i, _i, _i, I3, I3, I3, _i], ctypes.c_size_t),
+        "na_topk_tiles": ([I3, _i, _i, I3, I3], _i),
+        "na_topk_workspace_bytes": ([_i, _i, _i, I3, _i, _i], ctypes.c_size_t),
+        "na_topk_select": ([_p, _p, _i, _i, _i, I3, _i, _i, _p, _p, _p, ctypes.c_size_t, _p], _i),
+        "na_topk_forward": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, _i, ctypes.c_float, _i, _p, ctypes.c_size_t, _p],
+                            _i),
         "na_backward": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _p,
                          ctypes.c_size_t, _p], _i),
     }
@@ -319,6 +325,55 @@ def forward(q, k, v, window, stride=1, scale=None, qkv_scale=None, return_lse=Tr
     [B, *grid, heads] fp32 (None if return_lse is False)."""
     f = Forward(q, k, v, window, stride, scale, qkv_scale, return_lse, workspace)
     return f(stream)
+
+
+def na_topk_tiles(grid, head_dim, dtype):
+    tq, tk = I3(), I3()
+    _check(load().na_topk_tiles(_i3(grid), head_dim, dtype, tq, tk))
+    return tuple(tq), tuple(tk)
+
+
+def na_topk_workspace_bytes(batch, heads, head_dim, grid, keep, dtype) -> int:
+    n = load().na_topk_workspace_bytes(batch, heads, head_dim, _i3(grid), keep, dtype)
+    if n == 0 and batch > 0 and heads > 0:
+        raise NAError(NA_ERR_INVALID_ARG, na_last_error())
+    return n
+
+
+def topk_select(q, k, keep, stream=None):
+    """Content-selected tile map of q, k (bf16 device tensors [B, *grid,
+    heads, D]): (kv_idx [B*heads, nQ, keep], n_full [B*heads, nQ]) int32."""
+    torch = _torch()
+    grid = grid_of(q)
+    B, heads, D = q.shape[0], q.shape[-2], q.shape[-1]
+    dt = dtype_code(q.dtype)
+    tq, tk = na_topk_tiles(grid, D, dt)
+    nq = math.prod(-(-L // t) for L, t in zip(grid, tq))
+    nb = na_topk_workspace_bytes(B, heads, D, grid, keep, dt)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    idx = torch.empty((B * heads, nq, keep), dtype=torch.int32, device=q.device)
+    nf = torch.empty((B * heads, nq), dtype=torch.int32, device=q.device)
+    _check(load().na_topk_select(q.data_ptr(), k.data_ptr(), B, heads, D, _i3(grid), keep, dt, idx.data_ptr(),
+                                 nf.data_ptr(), ws.data_ptr(), nb, _stream_ptr(stream)))
+    return idx, nf
+
+
+def topk_forward(q, k, v, keep, scale=None, return_lse=True, stream=None):
+    """Attention of every query over the `keep` KV tiles its Q tile selects
+    (block-mean scores): (out, lse) like ``forward``."""
+    torch = _torch()
+    grid = grid_of(q)
+    B, heads, D = q.shape[0], q.shape[-2], q.shape[-1]
+    dt = dtype_code(q.dtype)
+    scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
+    nb = na_topk_workspace_bytes(B, heads, D, grid, keep, dt)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if return_lse else None
+    _check(load().na_topk_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, heads, D, _i3(grid), keep, scale,
+                                  dt, ws.data_ptr(), nb, _stream_ptr(stream)))
+    return out, lse
 
 
 def backward(q, k, v, out, lse, dout, window, stride=1, scale=None, stream=None):

@@ -162,9 +162,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   cint* qptr = (cint*)p.qptr;
   cint* kv_idx = (cint*)p.kv_idx;
   const int qrow_u = __builtin_amdgcn_readfirstlane(wi.qrow);
-  const int beg = __builtin_amdgcn_readfirstlane(qptr[qrow_u]);
-  const int end = __builtin_amdgcn_readfirstlane(qptr[qrow_u + 1]);
-  const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u]);
+  const int bh_u = __builtin_amdgcn_readfirstlane(wi.bh);
+  const int kvo = (int)(bh_u * p.map_bh_kv);     // per-(batch, head) maps (else 0)
+  const int beg = __builtin_amdgcn_readfirstlane(qptr[qrow_u]) + kvo;
+  const int end = __builtin_amdgcn_readfirstlane(qptr[qrow_u + 1]) + kvo;
+  const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u + bh_u * p.map_bh_nf]);
   const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
   const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
   const float c2 = p.c2;

@@ -35,6 +35,8 @@ struct KParams {
   float c2;             // scale * log2(e)
   float v_scale;        // multiplies the output (fp8), else 1
   int heads;            // heads (grid-order addressing)
+  int64_t map_bh_kv;    // per-(batch, head) tile maps: kv_idx offset per bh
+  int map_bh_nf;        // and n_full offset per bh (0: one shared map)
 };
 
 // Backward kernels' argument block (see BwdArgs).
@@ -87,6 +89,8 @@ inline KParams make_kparams(const AttnArgs& a) {
   p.c2 = fmaxf(a.scale * 1.4426950408889634f, 1e-30f);
   p.v_scale = a.v_scale;
   p.heads = a.heads;
+  p.map_bh_kv = a.map_bh_kv;
+  p.map_bh_nf = a.map_bh_nf;
   return p;
 }
 

@@ -28,6 +28,11 @@ struct AttnArgs {
   float scale;             // multiplies q.k (fp8: includes the q and k scales)
   float v_scale;           // fp8: multiplies the output; else 1
   int io_mode;             // IO_TILE, IO_QO or IO_GRID (tensor layouts, see attn_bf16.hip)
+  // per-(batch, head) tile maps (bf16 kernel only): row a of (batch, head)
+  // bh lists kv_idx[qptr[a] + bh * map_bh_kv ..] and has n_full[a + bh *
+  // map_bh_nf] full tiles; both 0 for a map shared by every (batch, head)
+  int64_t map_bh_kv;
+  int map_bh_nf;
 };
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
@@ -66,6 +71,31 @@ struct BwdArgs {
 };
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 bool attn_bwd_supported(int head_dim, int q_tokens, int kv_tokens);
+
+// Content-selected block sparsity: geometry of the pooling / selection
+// kernels and their buffers.  q and k are the caller's grid-order bf16
+// tensors; qm [B*heads, nq, D] and km [B*heads, nk, D] fp32 scratch for the
+// block means; kv_idx [B*heads, nq, keep], n_full [B*heads, nq] and
+// qptr [nq + 1] (the row starts a * keep) are the per-(batch, head) tile map.
+struct TopkGeom {
+  int batch, heads, head_dim;
+  int L[3];
+  int tq[3], tkv[3];
+};
+struct TopkArgs {
+  TopkGeom geom;
+  int nq, nk, keep;
+  const void* q;
+  const void* k;
+  float* qm;
+  float* km;
+  int32_t* kv_idx;
+  int32_t* n_full;
+  int32_t* qptr;
+};
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
+// LDS bytes of the selection kernel (must be <= 64 KiB).
+size_t select_lds_bytes(int nk, int head_dim);
 
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
 size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);

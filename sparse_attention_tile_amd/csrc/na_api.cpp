@@ -760,4 +760,170 @@ na_status na_backward(const void* q, const void* k, const void* v, const void* o
   return hip_status(na::launch_bwd(a, s), "backward launch");
 }
 
+// ---------------------------------------------------------------------------
+// content-selected block sparsity (top-k KV tiles per Q tile)
+
+namespace {
+
+struct TopkLayout {
+  int tq[3], tkv[3];
+  int nq, nk;
+  size_t off_qm, off_km, off_idx, off_nf, off_qptr, off_kt, off_vt, total;
+};
+
+na_status check_topk(int batch, int heads, int head_dim, const int grid[3], int keep, na_dtype dtype,
+                     TopkLayout* t) {
+  if (!grid) return fail(NA_ERR_INVALID_ARG, "grid must be non-null");
+  const int ones[3] = {1, 1, 1};
+  Layout lay;   // the blocks are the tiles of the dense geometry (window = grid)
+  na_status st = check_problem(batch, heads, head_dim, grid, grid, ones, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (dtype != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim))
+    return fail(NA_ERR_UNSUPPORTED, "top-k selection is built for bf16 with head_dim 64 or 128");
+  t->nq = lay.nq[0] * lay.nq[1] * lay.nq[2];
+  t->nk = lay.nk[0] * lay.nk[1] * lay.nk[2];
+  for (int d = 0; d < 3; ++d) {
+    t->tq[d] = lay.tq[d];
+    t->tkv[d] = lay.tkv[d];
+  }
+  if (keep < 1 || keep > t->nk) return fail(NA_ERR_INVALID_ARG, "keep must be in [1, number of KV tiles]");
+  if (na::select_lds_bytes(t->nk, head_dim) > 65536)
+    return fail(NA_ERR_UNSUPPORTED, "too many KV tiles for the selection kernel");
+  const size_t bh = (size_t)batch * heads;
+  if (bh * (size_t)t->nq * (size_t)keep >= (size_t(1) << 31))
+    return fail(NA_ERR_UNSUPPORTED, "tile map larger than 2^31 entries");
+  t->off_qm = 0;
+  t->off_km = t->off_qm + round256(bh * t->nq * head_dim * 4);
+  t->off_idx = t->off_km + round256(bh * t->nk * head_dim * 4);
+  t->off_nf = t->off_idx + round256(bh * t->nq * (size_t)keep * 4);
+  t->off_qptr = t->off_nf + round256(bh * t->nq * 4);
+  t->off_kt = t->off_qptr + round256(((size_t)t->nq + 1) * 4);
+  t->off_vt = t->off_kt + round256(lay.kv_bytes);
+  t->total = t->off_vt + round256(lay.kv_bytes);
+  return NA_OK;
+}
+
+na_status topk_select_impl(const void* q, const void* k, int batch, int heads, int head_dim, const int grid[3],
+                           int keep, const TopkLayout& t, char* ws, int32_t* kv_idx, int32_t* n_full,
+                           hipStream_t s) {
+  na::TopkArgs a{};
+  a.geom.batch = batch;
+  a.geom.heads = heads;
+  a.geom.head_dim = head_dim;
+  for (int d = 0; d < 3; ++d) {
+    a.geom.L[d] = grid[d];
+    a.geom.tq[d] = t.tq[d];
+    a.geom.tkv[d] = t.tkv[d];
+  }
+  a.nq = t.nq;
+  a.nk = t.nk;
+  a.keep = keep;
+  a.q = q;
+  a.k = k;
+  a.qm = reinterpret_cast<float*>(ws + t.off_qm);
+  a.km = reinterpret_cast<float*>(ws + t.off_km);
+  a.kv_idx = kv_idx;
+  a.n_full = n_full;
+  a.qptr = reinterpret_cast<int32_t*>(ws + t.off_qptr);
+  return hip_status(na::launch_topk_select(a, s), "top-k selection launch");
+}
+
+}  // namespace
+
+na_status na_topk_tiles(const int grid[3], int head_dim, na_dtype dtype, int tile_q[3], int tile_kv[3]) {
+  g_err.clear();
+  if (!tile_q || !tile_kv) return fail(NA_ERR_INVALID_ARG, "tile_q and tile_kv must be non-null");
+  TopkLayout t;
+  na_status st = check_topk(1, 1, head_dim, grid, 1, dtype, &t);
+  if (st != NA_OK) return st;
+  for (int d = 0; d < 3; ++d) {
+    tile_q[d] = t.tq[d];
+    tile_kv[d] = t.tkv[d];
+  }
+  return NA_OK;
+}
+
+size_t na_topk_workspace_bytes(int batch, int heads, int head_dim, const int grid[3], int keep, na_dtype dtype) {
+  g_err.clear();
+  TopkLayout t;
+  if (check_topk(batch, heads, head_dim, grid, keep, dtype, &t) != NA_OK) return 0;
+  return (batch == 0 || heads == 0) ? 0 : t.total;
+}
+
+na_status na_topk_select(const void* q, const void* k, int batch, int heads, int head_dim, const int grid[3],
+                         int keep, na_dtype dtype, int32_t* kv_idx, int32_t* n_full, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TopkLayout t;
+  na_status st = check_topk(batch, heads, head_dim, grid, keep, dtype, &t);
+  if (st != NA_OK) return st;
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!q || !k || !kv_idx || !n_full) return fail(NA_ERR_INVALID_ARG, "q, k, kv_idx and n_full must be non-null");
+  if (!aligned16(q) || !aligned16(k)) return fail(NA_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(kv_idx) | reinterpret_cast<uintptr_t>(n_full)) & 3u)
+    return fail(NA_ERR_INVALID_ARG, "kv_idx and n_full must be 4-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null and aligned");
+  if (workspace_bytes < t.total)
+    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(t.total) + " bytes");
+  return topk_select_impl(q, k, batch, heads, head_dim, grid, keep, t, static_cast<char*>(workspace), kv_idx, n_full,
+                          (hipStream_t)stream);
+}
+
+na_status na_topk_forward(const void* q, const void* k, const void* v, void* out, float* lse, int batch, int heads,
+                          int head_dim, const int grid[3], int keep, float scale, na_dtype dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  TopkLayout t;
+  na_status st = check_topk(batch, heads, head_dim, grid, keep, dtype, &t);
+  if (st != NA_OK) return st;
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!q || !k || !v || !out) return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  st = check_scales(scale, dtype, nullptr);
+  if (st != NA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return fail(NA_ERR_INVALID_ARG, "workspace must be non-null and aligned");
+  if (workspace_bytes < t.total)
+    return fail(NA_ERR_WORKSPACE, "workspace too small: need " + std::to_string(t.total) + " bytes");
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* kv_idx = reinterpret_cast<int32_t*>(ws + t.off_idx);
+  int32_t* n_full = reinterpret_cast<int32_t*>(ws + t.off_nf);
+  st = topk_select_impl(q, k, batch, heads, head_dim, grid, keep, t, ws, kv_idx, n_full, s);
+  if (st != NA_OK) return st;
+  void* kt = ws + t.off_kt;
+  void* vt = ws + t.off_vt;
+  if ((st = hip_status(na::launch_permute(k, kt, batch, heads, head_dim, grid, t.tkv, 2, 0, s), "permute k")) ||
+      (st = hip_status(na::launch_permute(v, vt, batch, heads, head_dim, grid, t.tkv, 2, 1, s), "permute v")))
+    return st;
+  na::AttnArgs a{};
+  a.qt = q;
+  a.kt = kt;
+  a.vt = vt;
+  a.ot = out;
+  a.lse_t = lse;
+  a.qptr = reinterpret_cast<int32_t*>(ws + t.off_qptr);
+  a.kv_idx = kv_idx;
+  a.n_full = n_full;
+  a.batch = batch;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  for (int d = 0; d < 3; ++d) {
+    a.L[d] = grid[d];
+    a.w[d] = grid[d];   // window = grid: the mask keeps every real key of a listed tile
+    a.s[d] = 1;
+    a.tq[d] = t.tq[d];
+    a.tkv[d] = t.tkv[d];
+    a.nq[d] = na::ceil_div(grid[d], t.tq[d]);
+    a.nk[d] = na::ceil_div(grid[d], t.tkv[d]);
+  }
+  a.scale = scale;
+  a.v_scale = 1.0f;
+  a.io_mode = na::IO_QO;
+  a.map_bh_kv = (int64_t)t.nq * keep;
+  a.map_bh_nf = t.nq;
+  return hip_status(na::launch_attn_bf16(a, s), "top-k attention launch");
+}
+
 }  // extern "C"

@@ -1,0 +1,141 @@
+// Content-selected block sparsity: block-mean importance scores and the
+// top-k KV tiles of every Q tile ("Video-generation inference speed-up:
+// sparse attention configuration tutorial", section 6: score blocks, keep the
+// most important ones by a keep ratio, skip the rest whole; "Sparse
+// attention: the key technology for more efficient AI models", section 2.2:
+// top-k selection).  The attention over the kept tiles is the bf16 GNA kernel
+// with one tile map per (batch, head).
+//
+// The selection is an integer decision taken from floating-point scores; it
+// is evaluated in one fixed float32 order (sequential sums with explicit
+// round-to-nearest adds and multiplies, no fused multiply-add, IEEE
+// division), so that it is reproducible bit for bit.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace na {
+namespace {
+
+// Mean over the real tokens of each tile of x (grid order [B, T, H, W,
+// heads, D] bf16) in in-tile row-major order: one thread per (tile, d) of a
+// (batch, head); out [B*heads, n_tiles, D] fp32.
+__global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restrict__ x, float* __restrict__ out,
+                                                         TopkGeom g, int t0, int t1, int t2, int64_t n_items) {
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (bh, tile, d)
+  if (item >= n_items) return;
+  const int d = (int)(item % g.head_dim);
+  const int64_t bt = item / g.head_dim;
+  const int nt1 = (g.L[1] + t1 - 1) / t1, nt2 = (g.L[2] + t2 - 1) / t2;
+  const int ntl = ((g.L[0] + t0 - 1) / t0) * nt1 * nt2;
+  const int tile = (int)(bt % ntl);
+  const int bh = (int)(bt / ntl);
+  const int b = bh / g.heads, h = bh % g.heads;
+  const int a2 = tile % nt2, a1 = (tile / nt2) % nt1, a0 = tile / (nt2 * nt1);
+  const int64_t N = (int64_t)g.L[0] * g.L[1] * g.L[2];
+  float acc = 0.f;
+  int cnt = 0;
+  for (int dt = 0; dt < t0; ++dt) {
+    const int t = a0 * t0 + dt;
+    if (t >= g.L[0]) break;
+    for (int dy = 0; dy < t1; ++dy) {
+      const int y = a1 * t1 + dy;
+      if (y >= g.L[1]) break;
+      for (int dx = 0; dx < t2; ++dx) {
+        const int xx = a2 * t2 + dx;
+        if (xx >= g.L[2]) break;
+        const int64_t tok = ((int64_t)t * g.L[1] + y) * g.L[2] + xx;
+        acc = __fadd_rn(acc, (float)x[((b * N + tok) * g.heads + h) * g.head_dim + d]);
+        ++cnt;
+      }
+    }
+  }
+  out[item] = __fdiv_rn(acc, (float)cnt);
+}
+
+// Top-k KV tiles of one Q tile of one (batch, head): scores in LDS, then each
+// candidate's rank = #{c' : s' > s or (s' == s and c' < c)}; the keep
+// best are written full tiles first, then tiles with padding, each
+// ascending.  qptr (shared by all (batch, head)) is written by bh 0.
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qm, const float* __restrict__ km,
+                                                     int32_t* __restrict__ kv_idx, int32_t* __restrict__ n_full,
+                                                     int32_t* __restrict__ qptr, TopkGeom g, int nq, int nk,
+                                                     int keep) {
+  extern __shared__ float sh[];
+  float* sc = sh;                                    // [nk] scores
+  float* qv = sh + nk;                               // [head_dim] this Q tile's mean
+  unsigned char* sel = reinterpret_cast<unsigned char*>(qv + g.head_dim);   // [nk] 1 = kept
+  __shared__ int n_kept_full;
+  const int row = blockIdx.x;                        // bh * nq + a
+  const int bh = row / nq, a = row % nq;
+  const int D = g.head_dim;
+  for (int d = threadIdx.x; d < D; d += 256) qv[d] = qm[(int64_t)row * D + d];
+  if (threadIdx.x == 0) n_kept_full = 0;
+  __syncthreads();
+  const float* kb = km + (int64_t)bh * nk * D;
+  for (int c = threadIdx.x; c < nk; c += 256) {
+    float s = 0.f;
+    for (int d = 0; d < D; ++d) s = __fadd_rn(s, __fmul_rn(qv[d], kb[(int64_t)c * D + d]));
+    sc[c] = s;
+  }
+  __syncthreads();
+  // KV tile c has no padding slot iff its last row/column/frame is inside the grid
+  const int nt1 = (g.L[1] + g.tkv[1] - 1) / g.tkv[1], nt2 = (g.L[2] + g.tkv[2] - 1) / g.tkv[2];
+  auto full_tile = [&](int c) {
+    const int c2 = c % nt2, c1 = (c / nt2) % nt1, c0 = c / (nt2 * nt1);
+    return (c0 + 1) * g.tkv[0] <= g.L[0] && (c1 + 1) * g.tkv[1] <= g.L[1] && (c2 + 1) * g.tkv[2] <= g.L[2];
+  };
+  for (int c = threadIdx.x; c < nk; c += 256) {
+    const float s = sc[c];
+    int rank = 0;
+    for (int c2 = 0; c2 < nk; ++c2) {
+      const float t = sc[c2];
+      rank += (t > s) || (t == s && c2 < c);
+    }
+    const bool kept = rank < keep;
+    sel[c] = kept ? 1 : 0;
+    if (kept && full_tile(c)) atomicAdd(&n_kept_full, 1);
+  }
+  __syncthreads();
+  const int nf = n_kept_full;
+  int32_t* out = kv_idx + (int64_t)row * keep;
+  for (int c = threadIdx.x; c < nk; c += 256) {
+    if (!sel[c]) continue;
+    const bool f = full_tile(c);
+    int pos = f ? 0 : nf;
+    for (int c2 = 0; c2 < c; ++c2) pos += sel[c2] && (full_tile(c2) == f);
+    out[pos] = c;
+  }
+  if (threadIdx.x == 0) {
+    n_full[row] = nf;
+    if (bh == 0) {
+      qptr[a] = a * keep;
+      if (a == nq - 1) qptr[nq] = nq * keep;
+    }
+  }
+}
+
+}  // namespace
+
+size_t select_lds_bytes(int nk, int head_dim) { return (size_t)nk * 4 + (size_t)head_dim * 4 + (size_t)nk + 16; }
+
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
+  const TopkGeom& g = a.geom;
+  const int64_t bh = (int64_t)g.batch * g.heads;
+  const int64_t nq_items = bh * a.nq * g.head_dim, nk_items = bh * a.nk * g.head_dim;
+  block_mean_kernel<<<(unsigned)((nq_items + 255) / 256), 256, 0, st>>>(static_cast<const __bf16*>(a.q), a.qm, g,
+                                                                          g.tq[0], g.tq[1], g.tq[2], nq_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  block_mean_kernel<<<(unsigned)((nk_items + 255) / 256), 256, 0, st>>>(static_cast<const __bf16*>(a.k), a.km, g,
+                                                                          g.tkv[0], g.tkv[1], g.tkv[2], nk_items);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  select_kernel<<<(unsigned)(bh * a.nq), 256, select_lds_bytes(a.nk, g.head_dim), st>>>(
+      a.qm, a.km, a.kv_idx, a.n_full, a.qptr, g, a.nq, a.nk, a.keep);
+  return hipGetLastError();
+}
+
+}  // namespace na

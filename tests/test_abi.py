@@ -207,3 +207,26 @@ def test_backward_arguments_rejected(na):
     a = na.na_backward_workspace_bytes(1, 2, 128, (1, 64, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
     b = na.na_backward_workspace_bytes(1, 2, 128, (1, 128, 64), (1, 9, 9), (1, 1, 1), na.NA_BF16)
     assert 1.9 < b / a < 2.1
+
+
+def test_topk_arguments_rejected(na):
+    lib = na.load()
+    I3 = na.I3
+    g = I3(1, 64, 64)
+    fake = 1 << 20
+    tq, tk = na.na_topk_tiles((1, 64, 64), 64, na.NA_BF16)
+    nk = math.prod(-(-L // t) for L, t in zip((1, 64, 64), tk))
+    ws = na.na_topk_workspace_bytes(1, 2, 64, (1, 64, 64), 5, na.NA_BF16)
+    assert ws > 0
+
+    def fwd(keep=5, dt=na.NA_BF16, D=64, ws_bytes=ws, q=fake):
+        return lib.na_topk_forward(q, fake, fake, fake, None, 1, 2, D, g, keep, 0.125, dt, fake, ws_bytes, None)
+
+    assert fwd(dt=na.NA_F32, D=32) == na.NA_ERR_UNSUPPORTED
+    assert fwd(keep=0) == na.NA_ERR_INVALID_ARG and fwd(keep=nk + 1) == na.NA_ERR_INVALID_ARG
+    assert fwd(q=None) == na.NA_ERR_INVALID_ARG
+    assert fwd(ws_bytes=ws - 1) == na.NA_ERR_WORKSPACE
+    assert lib.na_topk_select(fake, fake, 1, 2, 64, g, 5, na.NA_BF16, None, fake, fake, ws, None) == \
+        na.NA_ERR_INVALID_ARG
+    # the tile map part of the workspace grows with keep
+    assert na.na_topk_workspace_bytes(1, 2, 64, (1, 64, 64), nk, na.NA_BF16) > ws
