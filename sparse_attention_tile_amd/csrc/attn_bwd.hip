@@ -89,8 +89,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dq: Q tile of NW * 32 queries, KV tiles of KVT keys.
-template <int D, int NW, int KVT>
+// dq: Q tile of NW * 32 queries, KV tiles of KVT keys.  GQ: q, dout, out
+// and lse are read in grid order and D_i is formed here from the dout and
+// out rows (no prep data needed); else q, dout come in tile order with the
+// prep kernel's lse2 / D.
+template <int D, int NW, int KVT, bool GQ>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdParams bp) {
   const KParams& p = bp.kp;
   constexpr int QT = NW * 32;
@@ -117,18 +120,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdParams bp) {
   const bool q_valid = qc.t < p.L0 && qc.y < p.L1 && qc.x < p.L2;
 
   // q and dO rows of this lane's query (B operands), its statistics
+  const int bb = wi.bh / p.heads, hd = wi.bh % p.heads;
+  const size_t tok = ((size_t)min(qc.t, p.L0 - 1) * p.L1 + min(qc.y, p.L1 - 1)) * p.L2 + min(qc.x, p.L2 - 1);
+  const size_t grow = ((size_t)bb * p.L0 * p.L1 * p.L2 + tok) * p.heads + hd;   // grid-order row (clamped)
   bf16x8 qr[DC], dr[DC];
+  float lse2, dd;
   {
-    const bf16x8* qs = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.qt) + slot * D);
-    const bf16x8* ds = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(bp.dot) + slot * D);
+    const size_t r = GQ ? grow : slot;
+    const bf16x8* qs = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(GQ ? bp.q : p.qt) + r * D);
+    const bf16x8* ds = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(GQ ? bp.dout : bp.dot) + r * D);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       qr[c] = qs[2 * c + hh];
       dr[c] = ds[2 * c + hh];
     }
+    if constexpr (GQ) {
+      // D_i = <dout_i, out_i>: this lane half holds 64 (or 32) of the dims
+      const bf16x8* os = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(bp.out) + r * D);
+      float part = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const bf16x8 o = os[2 * c + hh];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part = fmaf((float)dr[c][j], (float)o[j], part);
+      }
+      dd = xhalf_sum(part);
+      lse2 = bp.lse[r] * kLog2e;
+    } else {
+      lse2 = bp.lse2_t[slot];
+      dd = bp.d_t[slot];
+    }
   }
-  const float lse2 = bp.lse2_t[slot];
-  const float dd = bp.d_t[slot];
   const float c2 = p.c2;
 
   f32x16 acc[DB];
@@ -166,7 +188,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdParams bp) {
       tile_to_lds<TILEB, NW>(nk, koff, nb, wv);
       tile_to_lds<TILEB, NW>(nv, koff, nb + TILEB, wv);
     }
-#pragma unroll
+    // 8-wave tiles keep the block loop rolled: two waves per SIMD leave 256
+    // registers, and unrolling hoists operand reads past that
+#pragma unroll(GQ ? 1 : KB)
     for (int kb = 0; kb < KB; ++kb) {
       f32x16 s = qk_block<D, ROWB>(Ks, kb, krow0, kswz, hh, qr);
       const f32x16 dp = qk_block<D, ROWB>(Vs, kb, krow0, kswz, hh, dr);
@@ -211,9 +235,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdParams bp) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!q_valid) return;
-  const int bb = wi.bh / p.heads, hd = wi.bh % p.heads;
-  const size_t tok = ((size_t)qc.t * p.L1 + qc.y) * p.L2 + qc.x;
-  __bf16* orow = static_cast<__bf16*>(bp.dq) + (((size_t)bb * p.L0 * p.L1 * p.L2 + tok) * p.heads + hd) * D;
+  __bf16* orow = static_cast<__bf16*>(bp.dq) + grow * D;
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
@@ -436,8 +458,13 @@ bool attn_bwd_supported(int head_dim, int q_tokens, int kv_tokens) {
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   const int qtok = a.attn.tq[0] * a.attn.tq[1] * a.attn.tq[2];
   const int ktok = a.attn.tkv[0] * a.attn.tkv[1] * a.attn.tkv[2];
-  if (!attn_bwd_supported(a.attn.head_dim, qtok, ktok) || a.attn.tq[2] < 8 || a.attn.tkv[2] < 8)
+  const int dq_q = a.dq_attn.tq[0] * a.dq_attn.tq[1] * a.dq_attn.tq[2];
+  if (!attn_bwd_supported(a.attn.head_dim, qtok, ktok) || a.attn.tq[2] < 8 || a.attn.tkv[2] < 8 ||
+      (dq_q != 128 && dq_q != 256))
     return hipErrorInvalidValue;
+  for (int d = 0; d < 3; ++d)
+    if (a.dq_attn.tkv[d] != a.attn.tkv[d] || (dq_q == 128 && a.dq_attn.tq[d] != a.attn.tq[d]))
+      return hipErrorInvalidValue;   // the dq kernel shares the tile-order k, v (and, at 128, q, dout)
   BwdParams p;
   p.kp = make_kparams(a.attn);
   p.dot = a.dot;
@@ -452,6 +479,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   p.tqptr = a.tqptr;
   p.tq_idx = a.tq_idx;
   p.tn_full = a.tn_full;
+  p.q = a.q;
   const int64_t rows = (int64_t)p.kp.num_wg * qtok;
   const bool d128 = a.attn.head_dim == 128;
   const int rpb = 256 / (a.attn.head_dim / 8);
@@ -462,10 +490,21 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
     bwd_prep_kernel<64><<<prep_blocks, 256, 0, st>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (d128)
-    bwd_dq_kernel<128, 4, 128><<<p.kp.num_wg, 256, 0, st>>>(p);
-  else
-    bwd_dq_kernel<64, 4, 128><<<p.kp.num_wg, 256, 0, st>>>(p);
+  // dq: over its own tile map (dq_attn); 256-query tiles read grid order
+  BwdParams pq = p;
+  pq.kp = make_kparams(a.dq_attn);
+  const int dq_qtok = a.dq_attn.tq[0] * a.dq_attn.tq[1] * a.dq_attn.tq[2];
+  if (dq_qtok == 256) {
+    if (d128)
+      bwd_dq_kernel<128, 8, 128, true><<<pq.kp.num_wg, 512, 0, st>>>(pq);
+    else
+      bwd_dq_kernel<64, 8, 128, true><<<pq.kp.num_wg, 512, 0, st>>>(pq);
+  } else {
+    if (d128)
+      bwd_dq_kernel<128, 4, 128, false><<<pq.kp.num_wg, 256, 0, st>>>(pq);
+    else
+      bwd_dq_kernel<64, 4, 128, false><<<pq.kp.num_wg, 256, 0, st>>>(pq);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   BwdParams pk = p;

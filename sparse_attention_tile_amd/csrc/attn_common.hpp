@@ -42,6 +42,7 @@ struct KParams {
 // Backward kernels' argument block (see BwdArgs).
 struct BwdParams {
   KParams kp;
+  const void* q;          // grid-order q (dq kernel reading grid order)
   const void* dot;
   const void* out;
   const void* dout;

@@ -56,6 +56,10 @@ bool attn_bf16_grid_io_supported(int head_dim);
 // map (per KV tile, its Q tiles, full ones first).
 struct BwdArgs {
   AttnArgs attn;
+  // the dq kernel's problem: its own tile map; KV tiles as attn's, Q tiles of
+  // 256 tokens (then q, dout, out, lse are read in grid order) or attn's
+  AttnArgs dq_attn;
+  const void* q;
   const void* dot;
   const void* out;
   const void* dout;
@@ -74,7 +78,7 @@ bool attn_bwd_supported(int head_dim, int q_tokens, int kv_tokens);
 
 // Content-selected block sparsity: geometry of the pooling / selection
 // kernels and their buffers.  q and k are the caller's grid-order bf16
-// tensors; qm [B*heads, nq, D] and km [B*heads, nk, D] fp32 scratch for the
+// tensors; qm [B*heads, nq, D] and km [B*heads, D, nk] fp32 scratch for the
 // block means; kv_idx [B*heads, nq, keep], n_full [B*heads, nq] and
 // qptr [nq + 1] (the row starts a * keep) are the per-(batch, head) tile map.
 struct TopkGeom {
@@ -94,7 +98,8 @@ struct TopkArgs {
   int32_t* qptr;
 };
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
-// LDS bytes of the selection kernel (must be <= 64 KiB).
+// 0 when the selection kernel handles (nk, head_dim) (nk <= 4096 tiles,
+// head_dim <= 128), else a value above any LDS size.
 size_t select_lds_bytes(int nk, int head_dim);
 
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).

@@ -649,6 +649,7 @@ namespace {
 // Tile shapes and tile-order buffers of one backward problem.
 struct BwdLayout {
   int tq[3], tkv[3];
+  int dq_tq[3];   // Q tiles of the dq kernel (256 tokens when a pair with these KV tiles exists, else tq)
   size_t q_bytes, kv_bytes, stat_bytes;
   size_t off_q, off_k, off_v, off_do, off_l, off_d, total;
 };
@@ -676,6 +677,14 @@ na_status check_bwd(int batch, int heads, int head_dim, const int grid[3], const
     break;
   }
   if (!found) return fail(NA_ERR_UNSUPPORTED, "no 128 x 128 tile pair at least 8 wide along W fits this grid");
+  // the dq kernel: the cheapest 256-query tile paired with the same KV tiles
+  // (8 waves, two per SIMD), else the 128-query tile
+  for (int d = 0; d < 3; ++d) b->dq_tq[d] = b->tq[d];
+  for (const auto& c : na::tile_candidates(g, head_dim, na::Family::MFMA16)) {
+    if (c.tq[0] * c.tq[1] * c.tq[2] != 256 || !std::equal(c.tkv, c.tkv + 3, b->tkv)) continue;
+    for (int d = 0; d < 3; ++d) b->dq_tq[d] = c.tq[d];
+    break;
+  }
   int64_t npq = 1, npk = 1;
   for (int d = 0; d < 3; ++d) {
     npq *= (int64_t)na::ceil_div(grid[d], b->tq[d]) * b->tq[d];
@@ -729,6 +738,9 @@ na_status na_backward(const void* q, const void* k, const void* v, const void* o
   Plan* plan = nullptr;
   st = get_plan_t(g, b.tq, b.tkv, &plan);
   if (st != NA_OK) return st;
+  Plan* plan_dq = nullptr;
+  st = get_plan(g, b.dq_tq, b.tkv, &plan_dq);
+  if (st != NA_OK) return st;
   char* ws = static_cast<char*>(workspace);
   hipStream_t s = (hipStream_t)stream;
   void* qt = ws + b.off_q;
@@ -745,6 +757,11 @@ na_status na_backward(const void* q, const void* k, const void* v, const void* o
   a.attn.qt = qt;
   a.attn.kt = kt;
   a.attn.vt = vt;
+  a.dq_attn = attn_args(g, plan_dq, b.dq_tq, b.tkv, batch, heads, head_dim, scale);
+  a.dq_attn.qt = qt;
+  a.dq_attn.kt = kt;
+  a.dq_attn.vt = vt;
+  a.q = q;
   a.dot = dot;
   a.out = out;
   a.dout = dout;

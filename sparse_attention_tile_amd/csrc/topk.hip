@@ -21,9 +21,11 @@ namespace {
 
 // Mean over the real tokens of each tile of x (grid order [B, T, H, W,
 // heads, D] bf16) in in-tile row-major order: one thread per (tile, d) of a
-// (batch, head); out [B*heads, n_tiles, D] fp32.
+// (batch, head); out [B*heads, n_tiles, D] fp32, or [B*heads, D, n_tiles]
+// with `dim_major` (the layout the selection reads K means in).
 __global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restrict__ x, float* __restrict__ out,
-                                                         TopkGeom g, int t0, int t1, int t2, int64_t n_items) {
+                                                         TopkGeom g, int t0, int t1, int t2, int64_t n_items,
+                                                         bool dim_major) {
   const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (bh, tile, d)
   if (item >= n_items) return;
   const int d = (int)(item % g.head_dim);
@@ -52,21 +54,31 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restric
       }
     }
   }
-  out[item] = __fdiv_rn(acc, (float)cnt);
+  out[dim_major ? ((int64_t)bh * g.head_dim + d) * ntl + tile : item] = __fdiv_rn(acc, (float)cnt);
 }
 
-// Top-k KV tiles of one Q tile of one (batch, head): scores in LDS, then each
-// candidate's rank = #{c' : s' > s or (s' == s and c' < c)}; the keep
-// best are written full tiles first, then tiles with padding, each
-// ascending.  qptr (shared by all (batch, head)) is written by bh 0.
+// Order-preserving map of a float32 score to uint32 (larger float -> larger
+// integer; callers turn -0 into +0 first so equal floats map equal).
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Top-k KV tiles of one Q tile of one (batch, head).  Scores go to LDS as
+// 64-bit keys (ordered score bits, then the inverted tile index), sorted
+// descending by a bitonic network of SORTN >= nk entries (padding keys 0),
+// so the first `keep` keys are the kept tiles: larger score first, the lower
+// index first among equal scores.  The kept tiles are written full tiles
+// first (no padding slot), then the others, each ascending.  qptr (shared by
+// all (batch, head)) is written by bh 0.
+template <int SORTN>
 __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ qm, const float* __restrict__ km,
                                                      int32_t* __restrict__ kv_idx, int32_t* __restrict__ n_full,
                                                      int32_t* __restrict__ qptr, TopkGeom g, int nq, int nk,
                                                      int keep) {
-  extern __shared__ float sh[];
-  float* sc = sh;                                    // [nk] scores
-  float* qv = sh + nk;                               // [head_dim] this Q tile's mean
-  unsigned char* sel = reinterpret_cast<unsigned char*>(qv + g.head_dim);   // [nk] 1 = kept
+  __shared__ uint64_t key[SORTN];
+  __shared__ float qv[128];
+  __shared__ unsigned char sel[SORTN];
   __shared__ int n_kept_full;
   const int row = blockIdx.x;                        // bh * nq + a
   const int bh = row / nq, a = row % nq;
@@ -74,29 +86,43 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
   for (int d = threadIdx.x; d < D; d += 256) qv[d] = qm[(int64_t)row * D + d];
   if (threadIdx.x == 0) n_kept_full = 0;
   __syncthreads();
-  const float* kb = km + (int64_t)bh * nk * D;
-  for (int c = threadIdx.x; c < nk; c += 256) {
-    float s = 0.f;
-    for (int d = 0; d < D; ++d) s = __fadd_rn(s, __fmul_rn(qv[d], kb[(int64_t)c * D + d]));
-    sc[c] = s;
+  const float* kb = km + (int64_t)bh * nk * D;       // [D][nk]: lanes read consecutive tiles
+  for (int c = threadIdx.x; c < SORTN; c += 256) {
+    uint64_t kk = 0;
+    if (c < nk) {
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = __fadd_rn(s, __fmul_rn(qv[d], kb[(int64_t)d * nk + c]));
+      s = __fadd_rn(s, 0.f);   // -0 -> +0: equal floats get equal keys
+      kk = ((uint64_t)ordered_bits(s) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)c);
+    }
+    key[c] = kk;
+    sel[c] = 0;
   }
   __syncthreads();
-  // KV tile c has no padding slot iff its last row/column/frame is inside the grid
+  // bitonic sort, descending
+  for (int size = 2; size <= SORTN; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < SORTN / 2; i += 256) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = key[lo], y = key[hi];
+        if ((x < y) == desc) {
+          key[lo] = y;
+          key[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
   const int nt1 = (g.L[1] + g.tkv[1] - 1) / g.tkv[1], nt2 = (g.L[2] + g.tkv[2] - 1) / g.tkv[2];
   auto full_tile = [&](int c) {
     const int c2 = c % nt2, c1 = (c / nt2) % nt1, c0 = c / (nt2 * nt1);
     return (c0 + 1) * g.tkv[0] <= g.L[0] && (c1 + 1) * g.tkv[1] <= g.L[1] && (c2 + 1) * g.tkv[2] <= g.L[2];
   };
-  for (int c = threadIdx.x; c < nk; c += 256) {
-    const float s = sc[c];
-    int rank = 0;
-    for (int c2 = 0; c2 < nk; ++c2) {
-      const float t = sc[c2];
-      rank += (t > s) || (t == s && c2 < c);
-    }
-    const bool kept = rank < keep;
-    sel[c] = kept ? 1 : 0;
-    if (kept && full_tile(c)) atomicAdd(&n_kept_full, 1);
+  for (int r = threadIdx.x; r < keep; r += 256) {
+    const int c = (int)(0xFFFFFFFFu - (uint32_t)(key[r] & 0xFFFFFFFFu));
+    sel[c] = 1;
+    if (full_tile(c)) atomicAdd(&n_kept_full, 1);
   }
   __syncthreads();
   const int nf = n_kept_full;
@@ -119,22 +145,29 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
 
 }  // namespace
 
-size_t select_lds_bytes(int nk, int head_dim) { return (size_t)nk * 4 + (size_t)head_dim * 4 + (size_t)nk + 16; }
+// Largest sortable tile count (the sort keys of a row live in LDS).
+constexpr int kMaxSort = 4096;
+size_t select_lds_bytes(int nk, int head_dim) {
+  return nk <= kMaxSort && head_dim <= 128 ? 0 : (size_t)1 << 30;   // static LDS; out of range otherwise
+}
 
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
   const TopkGeom& g = a.geom;
   const int64_t bh = (int64_t)g.batch * g.heads;
   const int64_t nq_items = bh * a.nq * g.head_dim, nk_items = bh * a.nk * g.head_dim;
   block_mean_kernel<<<(unsigned)((nq_items + 255) / 256), 256, 0, st>>>(static_cast<const __bf16*>(a.q), a.qm, g,
-                                                                          g.tq[0], g.tq[1], g.tq[2], nq_items);
+                                                                          g.tq[0], g.tq[1], g.tq[2], nq_items, false);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   block_mean_kernel<<<(unsigned)((nk_items + 255) / 256), 256, 0, st>>>(static_cast<const __bf16*>(a.k), a.km, g,
-                                                                          g.tkv[0], g.tkv[1], g.tkv[2], nk_items);
+                                                                          g.tkv[0], g.tkv[1], g.tkv[2], nk_items, true);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  select_kernel<<<(unsigned)(bh * a.nq), 256, select_lds_bytes(a.nk, g.head_dim), st>>>(
-      a.qm, a.km, a.kv_idx, a.n_full, a.qptr, g, a.nq, a.nk, a.keep);
+  const unsigned nb = (unsigned)(bh * a.nq);
+  if (a.nk <= 1024)
+    select_kernel<1024><<<nb, 256, 0, st>>>(a.qm, a.km, a.kv_idx, a.n_full, a.qptr, g, a.nq, a.nk, a.keep);
+  else
+    select_kernel<kMaxSort><<<nb, 256, 0, st>>>(a.qm, a.km, a.kv_idx, a.n_full, a.qptr, g, a.nq, a.nk, a.keep);
   return hipGetLastError();
 }
 
