@@ -115,24 +115,51 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
       __syncthreads();
     }
   const int nt1 = (g.L[1] + g.tkv[1] - 1) / g.tkv[1], nt2 = (g.L[2] + g.tkv[2] - 1) / g.tkv[2];
-  auto full_tile = [&](int c) {
-    const int c2 = c % nt2, c1 = (c / nt2) % nt1, c0 = c / (nt2 * nt1);
-    return (c0 + 1) * g.tkv[0] <= g.L[0] && (c1 + 1) * g.tkv[1] <= g.L[1] && (c2 + 1) * g.tkv[2] <= g.L[2];
-  };
+  // sel[c]: bit 0 kept, bit 1 kept and full (no padding slot)
   for (int r = threadIdx.x; r < keep; r += 256) {
     const int c = (int)(0xFFFFFFFFu - (uint32_t)(key[r] & 0xFFFFFFFFu));
-    sel[c] = 1;
-    if (full_tile(c)) atomicAdd(&n_kept_full, 1);
+    const int c2 = c % nt2, c1 = (c / nt2) % nt1, c0 = c / (nt2 * nt1);
+    const bool full =
+        (c0 + 1) * g.tkv[0] <= g.L[0] && (c1 + 1) * g.tkv[1] <= g.L[1] && (c2 + 1) * g.tkv[2] <= g.L[2];
+    sel[c] = full ? 3 : 1;
+  }
+  __syncthreads();
+  // positions: full kept tiles first, then the others, each ascending --
+  // an exclusive prefix count over c, each thread owning a run of SORTN/256
+  constexpr int RUN = SORTN / 256;
+  __shared__ int cnt_f[256], cnt_b[256];
+  int nfr = 0, nbr = 0;
+  const int c_lo = threadIdx.x * RUN;
+#pragma unroll
+  for (int e = 0; e < RUN; ++e) {
+    const unsigned char v = sel[c_lo + e];
+    nfr += v == 3;
+    nbr += v == 1;
+  }
+  cnt_f[threadIdx.x] = nfr;
+  cnt_b[threadIdx.x] = nbr;
+  __syncthreads();
+  if (threadIdx.x == 0) {   // 256-entry exclusive scan, one thread (cheap next to the sort)
+    int sf = 0, sb = 0;
+    for (int t = 0; t < 256; ++t) {
+      const int f = cnt_f[t], b = cnt_b[t];
+      cnt_f[t] = sf;
+      cnt_b[t] = sb;
+      sf += f;
+      sb += b;
+    }
+    n_kept_full = sf;
   }
   __syncthreads();
   const int nf = n_kept_full;
   int32_t* out = kv_idx + (int64_t)row * keep;
-  for (int c = threadIdx.x; c < nk; c += 256) {
-    if (!sel[c]) continue;
-    const bool f = full_tile(c);
-    int pos = f ? 0 : nf;
-    for (int c2 = 0; c2 < c; ++c2) pos += sel[c2] && (full_tile(c2) == f);
-    out[pos] = c;
+  int pf = cnt_f[threadIdx.x], pb = nf + cnt_b[threadIdx.x];
+#pragma unroll
+  for (int e = 0; e < RUN; ++e) {
+    const int c = c_lo + e;
+    const unsigned char v = sel[c];
+    if (v == 3) out[pf++] = c;
+    else if (v == 1) out[pb++] = c;
   }
   if (threadIdx.x == 0) {
     n_full[row] = nf;
