@@ -20,16 +20,19 @@ namespace na {
 namespace {
 
 // Mean over the real tokens of each tile of x (grid order [B, T, H, W,
-// heads, D] bf16) in in-tile row-major order: one thread per (tile, d) of a
-// (batch, head); out [B*heads, n_tiles, D] fp32, or [B*heads, D, n_tiles]
+// heads, D] bf16) in in-tile row-major order: one thread per (tile, 8 dims)
+// of a (batch, head), one 16-byte load per token, each dim's sum sequential
+// over the tokens; out [B*heads, n_tiles, D] fp32, or [B*heads, D, n_tiles]
 // with `dim_major` (the layout the selection reads K means in).
 __global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restrict__ x, float* __restrict__ out,
                                                          TopkGeom g, int t0, int t1, int t2, int64_t n_items,
                                                          bool dim_major) {
-  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (bh, tile, d)
+  typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (bh, tile, 8-dim chunk)
   if (item >= n_items) return;
-  const int d = (int)(item % g.head_dim);
-  const int64_t bt = item / g.head_dim;
+  const int chunks = g.head_dim / 8;
+  const int ch = (int)(item % chunks);
+  const int64_t bt = item / chunks;
   const int nt1 = (g.L[1] + t1 - 1) / t1, nt2 = (g.L[2] + t2 - 1) / t2;
   const int ntl = ((g.L[0] + t0 - 1) / t0) * nt1 * nt2;
   const int tile = (int)(bt % ntl);
@@ -37,7 +40,7 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restric
   const int b = bh / g.heads, h = bh % g.heads;
   const int a2 = tile % nt2, a1 = (tile / nt2) % nt1, a0 = tile / (nt2 * nt1);
   const int64_t N = (int64_t)g.L[0] * g.L[1] * g.L[2];
-  float acc = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int cnt = 0;
   for (int dt = 0; dt < t0; ++dt) {
     const int t = a0 * t0 + dt;
@@ -49,12 +52,19 @@ __global__ __launch_bounds__(256) void block_mean_kernel(const __bf16* __restric
         const int xx = a2 * t2 + dx;
         if (xx >= g.L[2]) break;
         const int64_t tok = ((int64_t)t * g.L[1] + y) * g.L[2] + xx;
-        acc = __fadd_rn(acc, (float)x[((b * N + tok) * g.heads + h) * g.head_dim + d]);
+        const bf16x8_t v = reinterpret_cast<const bf16x8_t*>(x + ((b * N + tok) * g.heads + h) * g.head_dim)[ch];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __fadd_rn(acc[j], (float)v[j]);
         ++cnt;
       }
     }
   }
-  out[dim_major ? ((int64_t)bh * g.head_dim + d) * ntl + tile : item] = __fdiv_rn(acc, (float)cnt);
+  const float fc = (float)cnt;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = ch * 8 + j;
+    out[dim_major ? ((int64_t)bh * g.head_dim + d) * ntl + tile : bt * g.head_dim + d] = __fdiv_rn(acc[j], fc);
+  }
 }
 
 // Order-preserving map of a float32 score to uint32 (larger float -> larger
@@ -181,7 +191,7 @@ size_t select_lds_bytes(int nk, int head_dim) {
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
   const TopkGeom& g = a.geom;
   const int64_t bh = (int64_t)g.batch * g.heads;
-  const int64_t nq_items = bh * a.nq * g.head_dim, nk_items = bh * a.nk * g.head_dim;
+  const int64_t nq_items = bh * a.nq * (g.head_dim / 8), nk_items = bh * a.nk * (g.head_dim / 8);
   block_mean_kernel<<<(unsigned)((nq_items + 255) / 256), 256, 0, st>>>(static_cast<const __bf16*>(a.q), a.qm, g,
                                                                           g.tq[0], g.tq[1], g.tq[2], nq_items, false);
   hipError_t e = hipGetLastError();
