@@ -318,7 +318,8 @@ na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt,
  * in float32 in a fixed order (token-by-token sums in in-tile row-major
  * order, IEEE division by the count, product-by-product sums over the head
  * dimension, no fused multiply-add), so the selection is reproducible bit
- * for bit.  bf16, head_dim 64 or 128; 1 <= keep <= number of KV tiles. */
+ * for bit.  bf16, head_dim 64 or 128; 1 <= keep <= number of KV tiles;
+ * at most 4096 KV tiles (else NA_ERR_UNSUPPORTED). */
 
 /* Tile (block) shapes top-k selection uses for this grid (host). */
 na_status na_topk_tiles(const int grid[3], int head_dim, na_dtype dtype,

@@ -98,9 +98,9 @@ struct TopkArgs {
   int32_t* qptr;
 };
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st);
-// 0 when the selection kernel handles (nk, head_dim) (nk <= 4096 tiles,
-// head_dim <= 128), else a value above any LDS size.
-size_t select_lds_bytes(int nk, int head_dim);
+// Whether the selection kernel handles nk KV tiles at head_dim (its sort
+// keys live in LDS: up to 4096 tiles).
+bool topk_select_supported(int nk, int head_dim);
 
 // LDS bytes the transposed permutation needs for one tile (must be <= 64 KiB).
 size_t permute_transpose_lds_bytes(int head_dim, int tile_tokens, int elem_bytes);

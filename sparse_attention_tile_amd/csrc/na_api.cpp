@@ -804,8 +804,8 @@ na_status check_topk(int batch, int heads, int head_dim, const int grid[3], int 
     t->tkv[d] = lay.tkv[d];
   }
   if (keep < 1 || keep > t->nk) return fail(NA_ERR_INVALID_ARG, "keep must be in [1, number of KV tiles]");
-  if (na::select_lds_bytes(t->nk, head_dim) > 65536)
-    return fail(NA_ERR_UNSUPPORTED, "too many KV tiles for the selection kernel");
+  if (!na::topk_select_supported(t->nk, head_dim))
+    return fail(NA_ERR_UNSUPPORTED, "more than 4096 KV tiles for the selection kernel");
   const size_t bh = (size_t)batch * heads;
   if (bh * (size_t)t->nq * (size_t)keep >= (size_t(1) << 31))
     return fail(NA_ERR_UNSUPPORTED, "tile map larger than 2^31 entries");

@@ -184,9 +184,7 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ q
 
 // Largest sortable tile count (the sort keys of a row live in LDS).
 constexpr int kMaxSort = 4096;
-size_t select_lds_bytes(int nk, int head_dim) {
-  return nk <= kMaxSort && head_dim <= 128 ? 0 : (size_t)1 << 30;   // static LDS; out of range otherwise
-}
+bool topk_select_supported(int nk, int head_dim) { return nk <= kMaxSort && head_dim <= 128 && head_dim % 8 == 0; }
 
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t st) {
   const TopkGeom& g = a.geom;
