@@ -197,7 +197,8 @@ def main():
 
     def attn_qo():
         na.na_attend_kv_tiled(q.data_ptr(), kt.data_ptr(), vt.data_ptr(), fwd.out.data_ptr(), fwd.lse.data_ptr(),
-                              B, H, D, wl.grid, wl.window, wl.stride, tk, wl.scale, dcode, stream)
+                              B, H, D, wl.grid, wl.window, wl.stride, tk, wl.scale, dcode, stream,
+                              qkv_scale=sc if fp8 else None)
 
     def stage_ms(fn):
         _, tot = time_steps(torch, fn, st_steps, 2)
@@ -212,6 +213,7 @@ def main():
         attn_qo_ms = stage_ms(attn_qo)
         stages["kv_copy_form"] = {"permute_kv": perm_kv_ms, "attention_q_out_grid_order": attn_qo_ms,
                                   "total": perm_kv_ms + attn_qo_ms}
+    if mode == 1 and dcode == na.NA_BF16:
         nw = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=False)
         stages["no_workspace_form"] = {"total": stage_ms(nw)}
         del nw

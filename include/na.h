@@ -183,7 +183,7 @@ size_t na_workspace_bytes(int batch, int heads, int head_dim,
 /* The form na_forward takes for this dtype and head_dim:
  *   0  permute q, k, v to tile order, tiled kernel, unpermute out and lse;
  *   1  permute k, v only; the kernel reads q and writes out and lse in grid
- *      order (bf16, head_dim 64 / 128, with a workspace);
+ *      order (bf16 with head_dim 64 / 128 and a workspace; fp8 with 128);
  *   2  no permutation and no workspace: the kernel also gathers the k / v
  *      tiles from grid order (bf16, head_dim 64 / 128, workspace NULL).
  * with_workspace says whether the call would pass a workspace.  The
@@ -211,7 +211,10 @@ void na_release_cache(void);
  *   the page plans to fuse away, section 2.2, does not exist).  Slower than
  *   the form above on the video workload (the token-by-token gather), but
  *   needs no memory beyond the outputs.
- *   fp32 and fp8: permute q, k, v to tile order (zero padding), run the tiled
+ *   fp8 (head_dim 128): as bf16 with a workspace -- permute k and v, the
+ *   kernel reads q and writes out and lse in grid order (a workspace is
+ *   required).
+ *   fp32: permute q, k, v to tile order (zero padding), run the tiled
  *   attention kernel, permute out and lse back to grid order.
  * na_forward_mode() tells which form a call takes.  When q is read in grid
  * order, the padding slots of ragged Q tiles read real tokens of the grid
@@ -292,18 +295,21 @@ na_status na_attend_tiled(const void* qt, const void* kt, const void* vt,
 /* The attention kernel of na_forward's form 1 alone (GNA page, sections 1.1
  * and 2.1-2.2): q, out and lse in grid order, k and v already in tile order
  * (as na_permute writes them: kt plain, vt transposed, both with tile_kv
- * tiles).  bf16 with head_dim 64 or 128 only (else NA_ERR_UNSUPPORTED).
+ * tiles).  bf16 with head_dim 64 or 128, or fp8 e4m3 with head_dim 128
+ * (else NA_ERR_UNSUPPORTED).
  *
- * q, out  device, [batch, T, H, W, heads, head_dim] bf16.
+ * q       device, [batch, T, H, W, heads, head_dim] in `dtype`.
+ * out     device, same shape, bf16.
  * lse     device, [batch, T, H, W, heads] fp32, or NULL.
  * tile_kv must be what na_choose_tiles returns for the problem.
- * Other arguments as for na_forward. */
+ * Other arguments (qkv_scale: fp8 dequantisation, NULL means 1, 1, 1) as
+ * for na_forward. */
 na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt,
                              void* out, float* lse, int batch, int heads,
                              int head_dim, const int grid[3],
                              const int window[3], const int stride[3],
                              const int tile_kv[3], float scale, na_dtype dtype,
-                             void* stream);
+                             const float* qkv_scale, void* stream);
 
 /* ---------------------------------------------------------------------- */
 /* Content-selected block sparsity (bf16).                                 */

@@ -90,7 +90,7 @@ def load():
         "na_unpermute_lse": ([_p, _p, _i, _i, I3, I3, _p], _i),
         "na_attend_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, I3, ctypes.c_float, _i, _fp,
                              _p], _i),
-        "na_attend_kv_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, ctypes.c_float, _i, _p], _i),
+        "na_attend_kv_tiled": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, I3, ctypes.c_float, _i, _fp, _p], _i),
         "na_backward_workspace_bytes": ([_i, _i, _i, I3, I3, I3, _i], ctypes.c_size_t),
         "na_topk_tiles": ([I3, _i, _i, I3, I3], _i),
         "na_topk_workspace_bytes": ([_i, _i, _i, I3, _i, _i], ctypes.c_size_t),
@@ -220,9 +220,10 @@ def na_attend_tiled(qt, kt, vt, ot, lse_t, batch, heads, head_dim, grid, window,
 
 
 def na_attend_kv_tiled(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, tile_kv, scale, dtype,
-                       stream):
+                       stream, qkv_scale=None):
+    qs = (ctypes.c_float * 3)(*qkv_scale) if qkv_scale is not None else None
     _check(load().na_attend_kv_tiled(q, kt, vt, out, lse, batch, heads, head_dim, _i3(grid), _i3(window),
-                                     _i3(stride), _i3(tile_kv), scale, dtype, stream))
+                                     _i3(stride), _i3(tile_kv), scale, dtype, qs, stream))
 
 
 def na_backward_workspace_bytes(batch, heads, head_dim, grid, window, stride, dtype) -> int:

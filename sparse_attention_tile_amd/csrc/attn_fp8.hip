@@ -44,7 +44,7 @@ constexpr float kLazyLog2 = 2.f;     // reference max moves when a block max exc
 // 16 h + 4 j + t, so accumulator i of lane half h holds key 16 h + i.
 __device__ __forceinline__ int kperm8(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
-__device__ __forceinline__ i32x8 lds_read32(const unsigned char* p0, const unsigned char* p1) {
+__device__ __forceinline__ i32x8 gload32(const unsigned char* p0, const unsigned char* p1) {
   const int4 a = *reinterpret_cast<const int4*>(p0);
   const int4 b = *reinterpret_cast<const int4*>(p1);
   return i32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -55,7 +55,10 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-template <int D, int NW, int KVT>
+// GQ: q, out and lse in grid order (each lane reads and writes its query's
+// row in place; padding rows read a clamped real token and store nothing),
+// k and v in tile order; else all in tile order.
+template <int D, int NW, int KVT, bool GQ>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   constexpr int QT = NW * 32;            // queries per workgroup
   constexpr int DS = D / 64;             // 64-dim k-steps of S^T
@@ -75,15 +78,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   const size_t qtile = (size_t)wi.bh * p.nQ + wi.qrow;
   const int row = wv * 32 + lq;
 
-  // ---- Q operand (B of S^T): query lq, dims 64 s + 32 hh .. + 31
-  i32x8 qr[DS];
-  {
-    const unsigned char* src = static_cast<const unsigned char*>(p.qt) + (qtile * QT + row) * D;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qr[s] = lds_read32(src + 64 * s + 32 * hh, src + 64 * s + 32 * hh + 16);
-  }
   int st0, st1, st2;
-  bool wave_active;
+  bool wave_active, q_valid;
+  int q_tok;                             // grid token of the query (clamped inside the grid)
   {
     const int px = row & ((1 << p.lq2) - 1);
     const int py = (row >> p.lq2) & ((1 << p.lq1) - 1);
@@ -92,7 +89,23 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     st0 = dev_window_start(gt, p.L0, p.w0, p.s0);
     st1 = dev_window_start(gy, p.L1, p.w1, p.s1);
     st2 = dev_window_start(gx, p.L2, p.w2, p.s2);
-    wave_active = __builtin_amdgcn_ballot_w64(gt < p.L0 && gy < p.L1 && gx < p.L2) != 0;
+    q_valid = gt < p.L0 && gy < p.L1 && gx < p.L2;
+    wave_active = __builtin_amdgcn_ballot_w64(q_valid) != 0;
+    q_tok = (min(gt, p.L0 - 1) * p.L1 + min(gy, p.L1 - 1)) * p.L2 + min(gx, p.L2 - 1);
+  }
+  // grid-order element offset of token 0 of this (batch, head) and the
+  // element stride between tokens (GQ)
+  const int bb = wi.bh / p.heads, hd = wi.bh % p.heads;
+  const size_t grid_base = ((size_t)bb * p.L0 * p.L1 * p.L2 * p.heads + hd) * D;
+  const size_t tok_stride = (size_t)p.heads * D;
+
+  // ---- Q operand (B of S^T): query lq, dims 64 s + 32 hh .. + 31
+  i32x8 qr[DS];
+  {
+    const unsigned char* src = static_cast<const unsigned char*>(p.qt) +
+                               (GQ ? grid_base + (size_t)q_tok * tok_stride : (qtile * QT + row) * D);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qr[s] = gload32(src + 64 * s + 32 * hh, src + 64 * s + 32 * hh + 16);
   }
 
   f32x16 o[DB];
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
 #pragma unroll
     for (int t = 0; t < DS; ++t) {
       const int c0 = 4 * t + 2 * hh;
-      const i32x8 a = lds_read32(kr + ((c0 ^ kswz) * 16), kr + (((c0 + 1) ^ kswz) * 16));
+      const i32x8 a = gload32(kr + ((c0 ^ kswz) * 16), kr + (((c0 + 1) ^ kswz) * 16));
       s = mfma8(a, qr[t], s);
     }
     return s;
@@ -188,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
       for (int d = 0; d < DB; ++d) {
         const unsigned char* vr = Vs + (d * 32 + lq) * VROW;
         const int c0 = 4 * st + hh, c1 = 4 * st + 2 + hh;
-        const i32x8 a = lds_read32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
+        const i32x8 a = gload32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
         o[d] = mfma8(a, pb, o[d]);
       }
       osum = mfma8(ones, pb, osum);
@@ -246,7 +259,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   // ---- epilogue: out = v_scale * O / l (the factor 64 of P cancels), bf16
   const float lt = wave_active ? osum[0] : 1.f;
   const float mult = p.v_scale / lt;
-  __bf16* orow = static_cast<__bf16*>(p.ot) + (qtile * QT + row) * D;
+  __bf16* orow = static_cast<__bf16*>(p.ot) + (GQ ? grid_base + (size_t)q_tok * tok_stride : (qtile * QT + row) * D);
+  if (GQ && !q_valid) return;            // padding rows have no place in grid order
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
 #pragma unroll
@@ -260,13 +274,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     }
   }
   if (p.lse_t && hh == 0)
-    p.lse_t[qtile * QT + row] =
+    p.lse_t[GQ ? (grid_base / D) + (size_t)q_tok * p.heads : qtile * QT + row] =
         m == -INFINITY ? 0.f : m * p.scale + logf(lt) - kPScaleLog2 * 0.69314718055994531f;
 }
 
 template <int NW, int KVT>
-hipError_t launch_cfg(const KParams& p, hipStream_t st) {
-  attn_fp8_kernel<128, NW, KVT><<<p.num_wg, NW * 64, 0, st>>>(p);
+hipError_t launch_cfg(const KParams& p, int io, hipStream_t st) {
+  if (io == IO_QO)
+    attn_fp8_kernel<128, NW, KVT, true><<<p.num_wg, NW * 64, 0, st>>>(p);
+  else
+    attn_fp8_kernel<128, NW, KVT, false><<<p.num_wg, NW * 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -280,13 +297,14 @@ hipError_t launch_attn_fp8(const AttnArgs& a, hipStream_t st) {
   const KParams p = make_kparams(a);
   const int qtok = a.tq[0] * a.tq[1] * a.tq[2];
   const int ktok = a.tkv[0] * a.tkv[1] * a.tkv[2];
-  if (!attn_fp8_supported(a.head_dim, qtok, ktok) || !attn_bf16_tile_ok(a.tkv)) return hipErrorInvalidValue;
+  if (!attn_fp8_supported(a.head_dim, qtok, ktok) || !attn_bf16_tile_ok(a.tkv) || a.io_mode == IO_GRID)
+    return hipErrorInvalidValue;
   const int key = (qtok == 256 ? 2 : 0) | (ktok == 128 ? 1 : 0);
   switch (key) {
-    case 0: return launch_cfg<4, 64>(p, st);
-    case 1: return launch_cfg<4, 128>(p, st);
-    case 2: return launch_cfg<8, 64>(p, st);
-    default: return launch_cfg<8, 128>(p, st);
+    case 0: return launch_cfg<4, 64>(p, a.io_mode, st);
+    case 1: return launch_cfg<4, 128>(p, a.io_mode, st);
+    case 2: return launch_cfg<8, 64>(p, a.io_mode, st);
+    default: return launch_cfg<8, 128>(p, a.io_mode, st);
   }
 }
 

@@ -224,12 +224,13 @@ na_status check_problem(int batch, int heads, int head_dim, const int grid[3], c
 }
 
 // Which form na_forward takes (the values of na_forward_mode): 0 permutes q,
-// k, v and unpermutes out, lse; 1 permutes k, v only (bf16: the kernel reads q
-// and writes out / lse in grid order); 2 permutes nothing (bf16 without a
-// workspace).  Test hook: NA_NO_FUSED=1 forces form 0.
+// k, v and unpermutes out, lse; 1 permutes k, v only (bf16 and fp8: the
+// kernel reads q and writes out / lse in grid order); 2 permutes nothing
+// (bf16 without a workspace).  Test hook: NA_NO_FUSED=1 forces form 0.
 int forward_mode(na_dtype dt, int head_dim, bool with_workspace) {
   const char* e = std::getenv("NA_NO_FUSED");
   if (e && e[0] == '1') return 0;
+  if (dt == NA_FP8_E4M3 && head_dim == 128) return 1;   // no permutation-free fp8 form: needs the workspace
   if (dt != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim)) return 0;
   return with_workspace ? 1 : 2;
 }
@@ -545,7 +546,8 @@ na_status na_attend_tiled(const void* qt, const void* kt, const void* vt, void* 
 
 na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt, void* out, float* lse, int batch,
                              int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
-                             const int tile_kv[3], float scale, na_dtype dtype, void* stream) {
+                             const int tile_kv[3], float scale, na_dtype dtype, const float* qkv_scale,
+                             void* stream) {
   g_err.clear();
   Layout lay;
   na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
@@ -553,16 +555,16 @@ na_status na_attend_kv_tiled(const void* q, const void* kt, const void* vt, void
   if (!tile_kv) return fail(NA_ERR_INVALID_ARG, "tile_kv must be non-null");
   for (int d = 0; d < 3; ++d)
     if (tile_kv[d] != lay.tkv[d]) return fail(NA_ERR_INVALID_ARG, "tile_kv differs from na_choose_tiles()");
-  if (dtype != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim))
-    return fail(NA_ERR_UNSUPPORTED, "grid-order q / out need bf16 with head_dim 64 or 128");
+  if (!((dtype == NA_BF16 && na::attn_bf16_grid_io_supported(head_dim)) || (dtype == NA_FP8_E4M3 && head_dim == 128)))
+    return fail(NA_ERR_UNSUPPORTED, "grid-order q / out need bf16 with head_dim 64 / 128 or fp8 with 128");
   if (batch == 0 || heads == 0) return NA_OK;
   if (!q || !kt || !vt || !out) return fail(NA_ERR_INVALID_ARG, "q, kt, vt and out must be non-null");
   if (!aligned16(q) || !aligned16(kt) || !aligned16(vt) || !aligned16(out))
     return fail(NA_ERR_INVALID_ARG, "q, kt, vt and out must be 16-byte aligned");
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  st = check_scales(scale, dtype, nullptr);
+  st = check_scales(scale, dtype, qkv_scale);
   if (st != NA_OK) return st;
-  return attend_impl(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, lay, scale, dtype, nullptr,
+  return attend_impl(q, kt, vt, out, lse, batch, heads, head_dim, grid, window, stride, lay, scale, dtype, qkv_scale,
                      na::IO_QO, (hipStream_t)stream);
 }
 

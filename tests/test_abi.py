@@ -104,8 +104,10 @@ def test_forward_mode_rule(na, monkeypatch):
         assert na.na_forward_mode(na.NA_BF16, D, True) == 1
         assert na.na_forward_mode(na.NA_BF16, D, False) == 2
     assert na.na_forward_mode(na.NA_BF16, 32, True) == 0
-    for dt in (na.NA_F32, na.NA_FP8_E4M3):
-        assert na.na_forward_mode(dt, 128, True) == 0 and na.na_forward_mode(dt, 128, False) == 0
+    assert na.na_forward_mode(na.NA_F32, 128, True) == 0 and na.na_forward_mode(na.NA_F32, 128, False) == 0
+    # fp8: grid-order q / out with k, v permuted; no form without a workspace
+    assert na.na_forward_mode(na.NA_FP8_E4M3, 128, True) == 1
+    assert na.na_forward_mode(na.NA_FP8_E4M3, 128, False) == 1
     monkeypatch.setenv("NA_NO_FUSED", "1")
     assert na.na_forward_mode(na.NA_BF16, 128, True) == 0 and na.na_forward_mode(na.NA_BF16, 128, False) == 0
 
@@ -117,6 +119,10 @@ def test_kv_copy_form_workspace(na, monkeypatch):
     padded = math.prod(-(-L // t) * t for L, t in zip(grid, tk))
     kv = 1 * 2 * padded * 128 * 2
     assert na.na_workspace_bytes(1, 2, 128, grid, window, stride, na.NA_BF16) == 2 * ((kv + 255) // 256 * 256)
+    # fp8 (one byte per element) takes the same form
+    tq8, tk8 = na.na_choose_tiles(grid, window, stride, 128, na.NA_FP8_E4M3)
+    kv8 = 1 * 2 * math.prod(-(-L // t) * t for L, t in zip(grid, tk8)) * 128
+    assert na.na_workspace_bytes(1, 2, 128, grid, window, stride, na.NA_FP8_E4M3) == 2 * ((kv8 + 255) // 256 * 256)
     monkeypatch.setenv("NA_NO_FUSED", "1")
     assert na.na_workspace_bytes(1, 2, 128, grid, window, stride, na.NA_BF16) > 2 * kv
 
@@ -148,14 +154,14 @@ def test_invalid_arguments_rejected(na, monkeypatch):
     assert fwd(scale=float("nan")) == na.NA_ERR_INVALID_ARG
     assert fwd(scale=-0.5) == na.NA_ERR_INVALID_ARG
     assert "scale" in na.na_last_error()
-    # the form-1 kernel entry point: bf16 only, tile_kv checked
+    # the form-1 kernel entry point: bf16 (head_dim 64 / 128) or fp8 (128), tile_kv checked
     tk = na.I3(*na.na_choose_tiles((1, 16, 16), (1, 5, 5), (1, 1, 1), 64, na.NA_BF16)[1])
     assert lib.na_attend_kv_tiled(fake, fake, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
-                                  good["stride"], tk, 0.125, na.NA_FP8_E4M3, None) == na.NA_ERR_UNSUPPORTED
+                                  good["stride"], tk, 0.125, na.NA_FP8_E4M3, None, None) == na.NA_ERR_UNSUPPORTED
     assert lib.na_attend_kv_tiled(fake, fake, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
-                                  good["stride"], I3(1, 1, 1), 0.125, na.NA_BF16, None) == na.NA_ERR_INVALID_ARG
+                                  good["stride"], I3(1, 1, 1), 0.125, na.NA_BF16, None, None) == na.NA_ERR_INVALID_ARG
     assert lib.na_attend_kv_tiled(fake, None, fake, fake, None, 1, 1, 64, good["grid"], good["window"],
-                                  good["stride"], tk, 0.125, na.NA_BF16, None) == na.NA_ERR_INVALID_ARG
+                                  good["stride"], tk, 0.125, na.NA_BF16, None, None) == na.NA_ERR_INVALID_ARG
     # permutation kernels
     assert lib.na_permute(fake, fake, 1, 1, 64, I3(1, 16, 16), I3(1, 3, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG
     assert lib.na_permute(fake, None, 1, 1, 64, I3(1, 16, 16), I3(1, 8, 8), 2, 0, None) == na.NA_ERR_INVALID_ARG

@@ -97,9 +97,10 @@ def test_predicted_time_behaves(na):
     assert (b["predicted_kernel_ms"] - launch) == pytest.approx(2 * (a["predicted_kernel_ms"] - launch), rel=0.05)
     f8 = na.na_simulate(1, 24, 128, g, w, s, na.NA_FP8_E4M3)
     assert f8["predicted_kernel_ms"] < a["predicted_kernel_ms"]
-    assert a["form"] == 1 and f8["form"] == 0
+    assert a["form"] == 1 and f8["form"] == 1
     assert a["predicted_forward_ms"] > a["predicted_kernel_ms"]   # the k / v permutes
-    assert f8["predicted_forward_ms"] - f8["predicted_kernel_ms"] > a["predicted_forward_ms"] - a["predicted_kernel_ms"] - 1e-9
+    # fp8 permutes the same k / v in one byte per element instead of two
+    assert 0 < f8["predicted_forward_ms"] - f8["predicted_kernel_ms"] < a["predicted_forward_ms"] - a["predicted_kernel_ms"]
     dense = na.na_simulate(1, 24, 128, g, g, (1, 1, 1), na.NA_BF16)
     assert dense["predicted_kernel_ms"] / a["predicted_kernel_ms"] == pytest.approx(a["speedup_bound"], rel=0.1)
 
