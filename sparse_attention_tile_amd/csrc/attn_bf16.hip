@@ -53,9 +53,11 @@ namespace {
 template <int DB>
 __device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, float& l, f32x16 (&o)[DB], float c2,
                                                   float thr) {
-  float bm = fmaxf(s[0], s[1]);
+  // one serial chain of three-input maxima (v_max3_f32: 8 instructions)
+  float bm = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
-  for (int i = 2; i < 16; i += 2) bm = fmaxf(bm, fmaxf(s[i], s[i + 1]));
+  for (int i = 3; i < 15; i += 2) bm = fmaxf(fmaxf(bm, s[i]), s[i + 1]);
+  bm = fmaxf(bm, s[15]);
   bm = xhalf_max(bm);
   if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {
     const float mn = fmaxf(m, bm);

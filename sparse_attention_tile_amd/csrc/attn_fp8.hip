@@ -168,9 +168,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
         apply_mask(s0, vmask, 2 * st);
         apply_mask(s1, vmask, 2 * st + 1);
       }
-      float bm = fmaxf(s0[0], s1[0]);
+      // one serial chain of three-input maxima (v_max3_f32)
+      float bm = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) bm = fmaxf(bm, fmaxf(s0[i], s1[i]));
+      for (int i = 1; i < 15; ++i) bm = fmaxf(fmaxf(bm, s1[i]), s0[i + 1]);
+      bm = fmaxf(bm, s1[15]);
       bm = xhalf_max(bm);
       if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {   // lazy rescaling, rare after the first steps
         const float mn = fmaxf(m, bm);
