@@ -170,6 +170,11 @@ bool tile_override(const char* var, int t[3]) {
   return true;
 }
 
+// One launch holds fewer than 2^32 work-items (the dispatch packet's grid
+// size is 32-bit); the largest kernels here use 512 threads per workgroup.
+constexpr int64_t kMaxWorkItems = int64_t(1) << 32;
+constexpr int kMaxThreadsPerWg = 512;
+
 // Sizes of the tile-ordered buffers of one problem.
 struct Layout {
   int tq[3], tkv[3];
@@ -200,13 +205,17 @@ na_status check_problem(int batch, int heads, int head_dim, const int grid[3], c
   const int ktok = lay->tkv[0] * lay->tkv[1] * lay->tkv[2];
   if (!kernel_supported(dt, head_dim, qtok, ktok) || (dt != NA_F32 && !na::attn_bf16_tile_ok(lay->tkv)))
     return fail(NA_ERR_UNSUPPORTED, "no kernel for this head_dim / tile combination");
-  int64_t npq = 1, npk = 1;
+  int64_t npq = 1, npk = 1, ntq = 1, ntk = 1;
   for (int d = 0; d < 3; ++d) {
     lay->nq[d] = na::ceil_div(grid[d], lay->tq[d]);
     lay->nk[d] = na::ceil_div(grid[d], lay->tkv[d]);
     npq *= (int64_t)lay->nq[d] * lay->tq[d];
     npk *= (int64_t)lay->nk[d] * lay->tkv[d];
+    ntq *= lay->nq[d];
+    ntk *= lay->nk[d];
   }
+  if ((int64_t)batch * heads * std::max(ntq, ntk) * kMaxThreadsPerWg >= kMaxWorkItems)
+    return fail(NA_ERR_UNSUPPORTED, "batch * heads * tiles too large for one launch (fewer than 2^23 workgroups)");
   const size_t bh = (size_t)batch * heads;
   const int eb = elem_bytes(dt);
   lay->q_bytes = bh * npq * head_dim * eb;
@@ -253,6 +262,11 @@ na_status check_tile_args(int batch, int heads, int head_dim, const int grid[3],
     return fail(NA_ERR_UNSUPPORTED, "head_dim * elem_bytes must be 16 times a power of two");
   const int64_t tt = (int64_t)tile[0] * tile[1] * tile[2];
   if (tt > 1024) return fail(NA_ERR_UNSUPPORTED, "more than 1024 tokens per tile");
+  if ((int64_t)grid[0] * grid[1] * grid[2] > (int64_t(1) << 30)) return fail(NA_ERR_UNSUPPORTED, "more than 2^30 tokens");
+  int64_t ntiles = 1;
+  for (int d = 0; d < 3; ++d) ntiles *= na::ceil_div(grid[d], tile[d]);
+  if ((int64_t)batch * heads * ntiles * 256 >= kMaxWorkItems)   // one 256-thread workgroup per tile
+    return fail(NA_ERR_UNSUPPORTED, "batch * heads * tiles too large for one launch");
   return NA_OK;
 }
 

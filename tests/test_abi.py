@@ -236,3 +236,24 @@ def test_topk_arguments_rejected(na):
         na.NA_ERR_INVALID_ARG
     # the tile map part of the workspace grows with keep
     assert na.na_topk_workspace_bytes(1, 2, 64, (1, 64, 64), nk, na.NA_BF16) > ws
+
+
+def test_launch_size_limits_rejected(na):
+    # one launch holds fewer than 2^32 work-items: problems beyond that (and
+    # grids beyond 2^30 tokens) are refused on the host before any launch
+    lib = na.load()
+    I3 = na.I3
+    fake = 1 << 20
+    big, one = I3(1, 32768, 32768), I3(1, 1, 1)
+    ws = 1 << 40
+
+    def fwd(heads):
+        return lib.na_forward(fake, fake, fake, fake, None, 1, heads, 128, big, one, one, 0.125, na.NA_BF16, None,
+                              fake, ws, None)
+
+    assert fwd(64) == na.NA_ERR_UNSUPPORTED and "launch" in na.na_last_error()
+    assert lib.na_permute(fake, fake, 1, 1, 128, big, I3(1, 8, 8), 2, 0, None) == na.NA_ERR_UNSUPPORTED
+    assert lib.na_permute(fake, fake, 1, 1, 128, I3(2, 32768, 32768), I3(1, 16, 16), 2, 0, None) == \
+        na.NA_ERR_UNSUPPORTED
+    assert lib.na_unpermute(fake, fake, 1, 1, 128, big, I3(1, 8, 8), 2, None) == na.NA_ERR_UNSUPPORTED
+    assert lib.na_workspace_bytes(1, 64, 128, big, one, one, na.NA_BF16) == 0

@@ -226,3 +226,32 @@ def test_three_forward_forms_agree(na, monkeypatch, grid):
             res[form] = _run(na, wl, q, k, v)
     for form in ("grid", "tiled"):
         assert torch.equal(res["qo"][0], res[form][0]) and torch.equal(res["qo"][1], res[form][1]), form
+
+
+def test_offsets_beyond_32_bits_match_the_small_problem(na, path):
+    # The video workload with every (batch, head) repeated: batch 2 x 168
+    # heads puts element offsets of q, k, v, out and of the tile-order copies
+    # above 2^32.  Each (b, h) is computed independently in one fixed order, so
+    # every copy must equal the 24-head original bit for bit (the original is
+    # the problem the full-size parity test checks against the oracle).
+    import gpu_util
+    wl = WORKLOADS["video_block"]
+    say(f"[special] 2 x 168 heads of the video workload ({path})")
+    _, _, _, _, q, k, v = inputs(wl)
+    ws = gpu_util.USE_WORKSPACE
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=ws)
+    out, lse = f()
+    torch.cuda.synchronize()
+    out, lse = out.clone(), lse.clone()
+    del f
+    rep = (2, 1, 1, 1, 7, 1)
+    qb, kb, vb = q.repeat(*rep), k.repeat(*rep), v.repeat(*rep)
+    assert qb.numel() > 2 ** 32
+    fb = na.Forward(qb, kb, vb, wl.window, wl.stride, scale=wl.scale, workspace=ws)
+    ob, lb = fb()
+    torch.cuda.synchronize()
+    for b, h in [(1, 167), (1, 150), (0, 161), (1, 0), (0, 71)]:
+        assert torch.equal(ob[b, ..., h, :], out[0, ..., h % wl.heads, :]), (b, h)
+        assert torch.equal(lb[b, ..., h], lse[0, ..., h % wl.heads]), (b, h)
+    del fb, qb, kb, vb, ob, lb
+    torch.cuda.empty_cache()
