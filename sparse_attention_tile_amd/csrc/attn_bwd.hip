@@ -26,6 +26,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <type_traits>
 
@@ -271,10 +272,27 @@ __device__ __forceinline__ void query_interval(int c, int L, int w, int s, int& 
   if (n < 0) n = 0;
 }
 
-template <int D, int NW, int QTT>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
+// What one wave of the dk/dv kernel does for its 32 keys: both gradients
+// (one wave per 32 keys), or one of them (two waves per 32 keys on one SIMD).
+// In the split the dV wave forms S and P = exp(S - lse) and passes P (bf16)
+// to its dK partner through LDS, so S is computed once; the dK wave forms
+// dP, dS = P (dP - D) and dK.  The split halves the registers a wave holds,
+// so two waves share each SIMD, and pairs the dV wave's exponentials with
+// the dK wave's dP product and the dK wave's dS arithmetic with the dV
+// product.  dS is formed from the bf16 P the PV product uses in all forms.
+enum DkdvRole { kBothKV = 0, kOnlyK = 1, kOnlyV = 2 };
+
+// One wave's share of a dk/dv workgroup: the NW waves of the workgroup copy
+// the Q-side tiles together; this wave owns keys kw * 32 .. kw * 32 + 31 of
+// the KW * 32-key tile.  px: the split's P exchange, [2 slots][KW][2][64
+// lanes] x 16 bytes.
+template <int D, int NW, int KW, int QTT, int ROLE>
+__device__ __forceinline__ void dkdv_wave(const BwdParams& bp, unsigned char* smem, unsigned char* px, int kw, int wv,
+                                          int lane) {
   const KParams& p = bp.kp;
-  constexpr int KT = NW * 32;           // keys per workgroup (the KV tile)
+  constexpr bool DOK = ROLE != kOnlyV, DOV = ROLE != kOnlyK;
+  constexpr bool NEED_K = ROLE != kOnlyK, NEED_V = ROLE != kOnlyV;   // k rows (for S), v rows (for dP)
+  constexpr int KT = KW * 32;           // keys per workgroup (the KV tile)
   constexpr int DC = D / 16;
   constexpr int DB = D / 32;
   constexpr int QB = QTT / 32;
@@ -283,11 +301,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
   constexpr int STATB = QTT * 4;        // lse or D of one Q tile
   constexpr int STAGE = 2 * TILEB + 2 * STATB;
   static_assert(QTT * 4 <= 64 * 16, "statistics copy is one wave instruction");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   lds_u8* lds = (lds_u8*)smem;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6), hh = lane >> 5, lq = lane & 31;
+  const int hh = lane >> 5, lq = lane & 31;
 
   // work item: (batch * heads, KV tile), KV tiles with T fastest, XCD remap
   const int n_wg = p.num_wg;
@@ -307,32 +322,34 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
   }
   const int kvrow = (c0 * p.nk1 + c1) * p.nk2 + c2;
   const size_t ktile = (size_t)bh * p.nK + kvrow;
-  const int row = wv * 32 + lq;
+  const int row = kw * 32 + lq;
   const Coord3 kc = slot_coord(row, c0, c1, c2, p.lk0, p.lk1, p.lk2);
   const bool k_valid = kc.t < p.L0 && kc.y < p.L1 && kc.x < p.L2;
-  int ql0, qn0, ql1, qn1, ql2, qn2;
-  query_interval(kc.t, p.L0, p.w0, p.s0, ql0, qn0);
-  query_interval(kc.y, p.L1, p.w1, p.s1, ql1, qn1);
-  query_interval(kc.x, p.L2, p.w2, p.s2, ql2, qn2);
+  int ql0 = 0, qn0 = 0, ql1 = 0, qn1 = 0, ql2 = 0, qn2 = 0;
+  if constexpr (NEED_K) {   // the mask belongs to the wave that forms P
+    query_interval(kc.t, p.L0, p.w0, p.s0, ql0, qn0);
+    query_interval(kc.y, p.L1, p.w1, p.s1, ql1, qn1);
+    query_interval(kc.x, p.L2, p.w2, p.s2, ql2, qn2);
+  }
 
-  bf16x8 kr[DC], vr[DC];
+  bf16x8 kr[NEED_K ? DC : 1], vr[NEED_V ? DC : 1];
   {
     const size_t slot = ktile * KT + row;
     const bf16x8* ks = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.kt) + slot * D);
     const bf16x8* vs = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(p.vt) + slot * D);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      kr[c] = ks[2 * c + hh];
-      vr[c] = vs[2 * c + hh];
+      if constexpr (NEED_K) kr[c] = ks[2 * c + hh];
+      if constexpr (NEED_V) vr[c] = vs[2 * c + hh];
     }
   }
   const float c2s = p.c2;
 
-  f32x16 ak[DB], av[DB];
+  f32x16 ak[DOK ? DB : 1], av[DOV ? DB : 1];
 #pragma unroll
   for (int d = 0; d < DB; ++d) {
-    ak[d] = f32x16{};
-    av[d] = f32x16{};
+    if constexpr (DOK) ak[d] = f32x16{};
+    if constexpr (DOV) av[d] = f32x16{};
   }
 
   typedef const __attribute__((address_space(4))) int32_t cint;
@@ -352,7 +369,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
   const int qrow0 = kperm(lq);
   const int qswz = swz<ROWB / 16>(qrow0);
 
-  // copy of one Q tile's rows, dO rows and statistics into a stage
+  // copy of one Q tile's rows, dO rows and statistics into a stage (all NW
+  // waves of the workgroup take part)
   auto copy_tile = [&](int a, lds_u8* st) {
     tile_to_lds<TILEB, NW>(qbase + (size_t)a * TILEB, qoff, st, wv);
     tile_to_lds<TILEB, NW>(dbase + (size_t)a * TILEB, qoff, st + TILEB, wv);
@@ -369,39 +387,52 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
                        bool copy, uint64_t vmask, auto bnd) {
     constexpr bool BOUNDARY = decltype(bnd)::value;
     if (copy) copy_tile(an, nb);
-#pragma unroll
+    // a split wave has half the registers: keep the query blocks rolled
+#pragma unroll(ROLE == kBothKV ? QB : 1)
     for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = qk_block<D, ROWB>(Qs, qb, qrow0, qswz, hh, kr);
-      const f32x16 dp = qk_block<D, ROWB>(Ds, qb, qrow0, qswz, hh, vr);
-      if constexpr (BOUNDARY) apply_mask(s, vmask, qb);
-      bf16x8 pv[2], dsv[2];
+      // this wave pair's P slot of the block: [c][lane], 16 bytes each
+      bf16x8* pslot = reinterpret_cast<bf16x8*>(px + ((qb & 1) * KW + kw) * 2048) + lane;
+      bf16x8 pv[2];
+      f32x16 dp;
+      if constexpr (DOK) dp = qk_block<D, ROWB>(Ds, qb, qrow0, qswz, hh, vr);
+      if constexpr (NEED_K) {
+        f32x16 s = qk_block<D, ROWB>(Qs, qb, qrow0, qswz, hh, kr);
+        if constexpr (BOUNDARY) apply_mask(s, vmask, qb);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        // accumulators 8c .. 8c+7 hold queries 32 qb + 16 c + 8 hh + 0..7
-        const int q0 = 32 * qb + 16 * c + 8 * hh;
-        float l8[8], d8[8];
+        for (int c = 0; c < 2; ++c) {
+          // accumulators 8c .. 8c+7 hold queries 32 qb + 16 c + 8 hh + 0..7
+          const int q0 = 32 * qb + 16 * c + 8 * hh;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          l8[e] = Ls[q0 + e];
-          d8[e] = Ss[q0 + e];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = 8 * c + e;
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[i], c2s, -l8[e]));
-          pv[c][e] = (__bf16)pr;
-          dsv[c][e] = (__bf16)(pr * (dp[i] - d8[e]));
+          for (int e = 0; e < 8; ++e) pv[c][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[8 * c + e], c2s, -Ls[q0 + e]));
         }
       }
+      if constexpr (ROLE == kOnlyV) {
+        pslot[0] = pv[0];
+        pslot[64] = pv[1];
+      }
+      if constexpr (ROLE != kBothKV) __syncthreads();   // the pair's P of this block is in LDS
+      if constexpr (ROLE == kOnlyK) {
+        pv[0] = pslot[0];
+        pv[1] = pslot[64];
+      }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 dsv;
+        if constexpr (DOK) {
+          const int q0 = 32 * qb + 16 * c + 8 * hh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsv[e] = (__bf16)((float)pv[c][e] * (dp[8 * c + e] - Ss[q0 + e]));
+        }
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          av[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_tr<D>(Ds, 32 * qb + 16 * c, d, lane), pv[c], av[d],
-                                                          0, 0, 0);
-          ak[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_tr<D>(Qs, 32 * qb + 16 * c, d, lane), dsv[c],
-                                                          ak[d], 0, 0, 0);
+          if constexpr (DOV)
+            av[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_tr<D>(Ds, 32 * qb + 16 * c, d, lane), pv[c],
+                                                            av[d], 0, 0, 0);
+          if constexpr (DOK)
+            ak[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand_tr<D>(Qs, 32 * qb + 16 * c, d, lane), dsv,
+                                                            ak[d], 0, 0, 0);
         }
+      }
     }
   };
 
@@ -416,7 +447,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
     const float* Ls = reinterpret_cast<const float*>(Qs + 2 * TILEB);
     const float* Ss = Ls + QTT;
     lds_u8* nb = lds + (stage ^ 1) * STAGE;
-    if (j < beg + nfull) {
+    if (!NEED_K || j < beg + nfull) {   // the dK wave of a split takes masked P from its partner
       tile_body(Qs, Qs + TILEB, Ls, Ss, nb, an, copy, 0ull, std::integral_constant<bool, false>{});
     } else {
       const int a2 = a % p.nq2, a1 = (a / p.nq2) % p.nq1, a0 = a / (p.nq2 * p.nq1);
@@ -432,21 +463,44 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
   const int bb = bh / p.heads, hd = bh % p.heads;
   const size_t tok = ((size_t)kc.t * p.L1 + kc.y) * p.L2 + kc.x;
   const size_t goff = (((size_t)bb * p.L0 * p.L1 * p.L2 + tok) * p.heads + hd) * D;
-  __bf16* krow = static_cast<__bf16*>(bp.dk) + goff;
-  __bf16* vrow = static_cast<__bf16*>(bp.dv) + goff;
 #pragma unroll
   for (int d = 0; d < DB; ++d)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      bf16x4 kv4, vv4;
+      if constexpr (DOK) {
+        bf16x4 kv4;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kv4[e] = (__bf16)(ak[d][4 * g + e] * p.scale);
-        vv4[e] = (__bf16)av[d][4 * g + e];
+        for (int e = 0; e < 4; ++e) kv4[e] = (__bf16)(ak[d][4 * g + e] * p.scale);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(bp.dk) + goff + d * 32 + 8 * g + 4 * hh) = kv4;
       }
-      *reinterpret_cast<bf16x4*>(krow + d * 32 + 8 * g + 4 * hh) = kv4;
-      *reinterpret_cast<bf16x4*>(vrow + d * 32 + 8 * g + 4 * hh) = vv4;
+      if constexpr (DOV) {
+        bf16x4 vv4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv4[e] = (__bf16)av[d][4 * g + e];
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(bp.dv) + goff + d * 32 + 8 * g + 4 * hh) = vv4;
+      }
     }
+}
+
+// SPLIT: 2 KW waves, one dK wave and one dV wave per 32 keys (waves w and
+// w + KW share keys; the hardware places them on the same SIMD); else KW = NW
+// waves doing both.
+template <int D, int NW, int QTT, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkdv_kernel(BwdParams bp) {
+  constexpr int KW = SPLIT ? NW / 2 : NW;
+  constexpr int STAGE = 2 * (QTT * D * 2) + 2 * (QTT * 4);
+  constexpr int PX = SPLIT ? 2 * KW * 2048 : 0;      // P exchange of the split
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + PX];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if constexpr (SPLIT) {
+    if (wv < KW)
+      dkdv_wave<D, NW, KW, QTT, kOnlyK>(bp, smem, smem + 2 * STAGE, wv, wv, lane);
+    else
+      dkdv_wave<D, NW, KW, QTT, kOnlyV>(bp, smem, smem + 2 * STAGE, wv - KW, wv, lane);
+  } else {
+    dkdv_wave<D, NW, KW, QTT, kBothKV>(bp, smem, nullptr, wv, wv, lane);
+  }
 }
 
 }  // namespace
@@ -509,10 +563,19 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   BwdParams pk = p;
   pk.kp.num_wg = a.attn.batch * a.attn.heads * p.kp.nK;
-  if (d128)
-    bwd_dkdv_kernel<128, 4, 128><<<pk.kp.num_wg, 256, 0, st>>>(pk);
-  else
-    bwd_dkdv_kernel<64, 4, 128><<<pk.kp.num_wg, 256, 0, st>>>(pk);
+  const char* e_split = std::getenv("NA_DKDV_SPLIT");
+  const bool split = !(e_split && e_split[0] == '0');
+  if (split) {
+    if (d128)
+      bwd_dkdv_kernel<128, 8, 128, true><<<pk.kp.num_wg, 512, 0, st>>>(pk);
+    else
+      bwd_dkdv_kernel<64, 8, 128, true><<<pk.kp.num_wg, 512, 0, st>>>(pk);
+  } else {
+    if (d128)
+      bwd_dkdv_kernel<128, 4, 128, false><<<pk.kp.num_wg, 256, 0, st>>>(pk);
+    else
+      bwd_dkdv_kernel<64, 4, 128, false><<<pk.kp.num_wg, 256, 0, st>>>(pk);
+  }
   return hipGetLastError();
 }
 

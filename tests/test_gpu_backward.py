@@ -46,10 +46,20 @@ SMALL = [
 ]
 
 
+@pytest.fixture(params=["split", "fused"])
+def dkdv(request, monkeypatch):
+    """The two dk/dv kernels: one wave per gradient and 32 keys (default), or
+    one wave for both (NA_DKDV_SPLIT=0)."""
+    if request.param == "fused":
+        monkeypatch.setenv("NA_DKDV_SPLIT", "0")
+    return request.param
+
+
 @pytest.mark.parametrize("name,kw", SMALL)
-def test_backward_small_all_rows(na, name, kw):
+def test_backward_small_all_rows(na, name, kw, dkdv):
     wl = WORKLOADS[name].with_(seed=900 + len(kw), **kw)
-    say(f"[bwd] {wl.name} grid={wl.grid} w={wl.window} s={wl.stride} D={wl.head_dim} B={wl.batch} H={wl.heads}")
+    say(f"[bwd] {wl.name} ({dkdv}) grid={wl.grid} w={wl.window} s={wl.stride} D={wl.head_dim} B={wl.batch} "
+        f"H={wl.heads}")
     qc, kc, vc, _ = make_qkv(wl, device="cpu")
     do = _dout(wl, wl.seed + 5)
     _, _, dq, dk, dv = _run(na, wl, qc.cuda(), kc.cuda(), vc.cuda(), do.cuda())
@@ -116,3 +126,18 @@ def test_backward_empty_batch(na):
     lse = torch.empty((0, 1, 16, 16, 2), dtype=torch.float32, device="cuda")
     dq, dk, dv = na.backward(e, e, e, e, lse, e, (1, 5, 5), (1, 1, 1))
     assert dq.shape == e.shape
+
+
+def test_dkdv_split_equals_fused_full_size(na, monkeypatch):
+    # the split kernel's dK and dV waves run the fused wave's arithmetic in the
+    # same order, so dk and dv agree bit for bit (here at full video size)
+    wl = WORKLOADS["video_block"]
+    qc, kc, vc, _ = make_qkv(wl, device="cpu")
+    do = _dout(wl, 4712).cuda()
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+    say("[bwd] dk/dv split vs fused, video block full size")
+    a = _run(na, wl, q, k, v, do)
+    monkeypatch.setenv("NA_DKDV_SPLIT", "0")
+    b = _run(na, wl, q, k, v, do)
+    for x, y in zip(a[2:], b[2:]):
+        assert torch.equal(x, y)
