@@ -254,6 +254,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     rescale_if_needed(s, m, l, o, c2, thr);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      // LLVM's single-wave MFMA / LDS-read interleaving strategy for this
+      // scheduling region (measured 1.5 % faster than the default order)
+      __builtin_amdgcn_iglp_opt(1);
       copy_step(nb, kb);
       f32x16 sn;
       if (kb + 1 < KB) sn = qk_block<D, KROW>(Ks, kb + 1, krow0, kswz, hh, qr);
