@@ -122,7 +122,12 @@ __device__ __forceinline__ WorkItem decode_work(const KParams& p, int bid) {
   const int nx = 8;
   const int q = p.num_wg / nx, r = p.num_wg % nx;
   const int x = bid % nx, loc = bid / nx;
-  const int logical = x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc;
+  // Window maps: each XCD takes one contiguous range, so Q tiles with the
+  // same KV list share an L2.  Per-(batch, head) content-selected maps have
+  // no such locality: there consecutive workgroups go to different XCDs, so
+  // the whole chip works on one head at a time and its K / V stay in the
+  // Infinity Cache (measured 2-4 % faster for top-k).
+  const int logical = p.map_bh_kv ? bid : (x < r ? x * (q + 1) + loc : r * (q + 1) + (x - r) * q + loc);
   WorkItem w;
   w.bh = logical / p.nQ;
   const int t = logical % p.nQ;
