@@ -281,8 +281,8 @@ bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tk
 //   at head_dim 64, 8.66 ms).
 double family_rate(Family fam, int head_dim) {
   switch (fam) {
-    case Family::MFMA16: return head_dim == 128 ? 1.11e15 : 0.90e15;
-    case Family::FP8: return 1.46e15;
+    case Family::MFMA16: return head_dim == 128 ? 1.15e15 : 0.90e15;
+    case Family::FP8: return 1.55e15;
     case Family::F32: return 4.3e13;
   }
   return 1e15;
