@@ -49,7 +49,20 @@
  * Errors.  Every entry point validates its arguments before launching
  * anything; on failure it returns a negative na_status, launches nothing and
  * leaves a message for na_last_error().  No entry point throws, prints or
- * aborts.
+ * aborts.  Problems whose launch would exceed 2^32 work-items (batch * heads
+ * * tiles * 512 threads), or grids of more than 2^30 tokens, are refused
+ * with NA_ERR_UNSUPPORTED.
+ *
+ * Test and tuning hooks (environment variables, read at each call; unset in
+ * normal use, and no hook changes a result beyond floating-point rounding):
+ *   NA_NO_FUSED=1       na_forward takes form 0 (see na_forward_mode);
+ *   NA_TILE_Q, NA_TILE_KV="t,h,w"  replace the chosen tile shapes (the kernel
+ *                       shape rules still apply; malformed -> INVALID_ARG);
+ *   NA_FORCE_MASK=1     every listed KV tile is treated as a boundary tile
+ *                       (results are bit-identical);
+ *   NA_DKDV_SPLIT=0     na_backward's dk/dv kernel runs one wave per 32 keys
+ *                       for both gradients instead of one wave per gradient
+ *                       (results are bit-identical).
  */
 #ifndef NA_H_
 #define NA_H_
