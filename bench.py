@@ -282,7 +282,7 @@ def main():
     torch_perm_ms = torch_permute_ms(torch, (q, k, v), wl.grid, (tq, tk, tk), st_steps)
 
     result = {
-        "metric": "effective TFLOP/s (unmasked FLOPs) of one GNA forward, 1 MI355X",
+        "metric": "effective TFLOP/s (unmasked FLOPs) & ms/call, % of MFMA peak, 1 MI355X",
         "value": eff / (ms * 1e-3) / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
