@@ -58,7 +58,13 @@ __device__ __forceinline__ f32x16 mfma8(const i32x8& a, const i32x8& b, const f3
 // GQ: q, out and lse in grid order (each lane reads and writes its query's
 // row in place; padding rows read a clamped real token and store nothing),
 // k and v in tile order; else all in tile order.
-template <int D, int NW, int KVT, bool GQ>
+//
+// PAIRED: the KV tiles in memory hold 64 keys, and two consecutive entries of
+// a tile-map row are loaded as one 128-key LDS tile (keys 0..63 from the
+// first, 64..127 from the second; a row with an odd count ends with a single
+// tile whose second half is masked).  One barrier then serves 128 keys
+// instead of 64.  A pair counts as full when both of its tiles are.
+template <int D, int NW, int KVT, bool GQ, bool PAIRED>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   constexpr int QT = NW * 32;            // queries per workgroup
   constexpr int DS = D / 64;             // 64-dim k-steps of S^T
@@ -66,9 +72,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   constexpr int NSTEP = KVT / 64;        // 64-key steps per KV tile
   constexpr int KROW = D;                // bytes per K row
   constexpr int VROW = KVT;              // bytes per V^T row
-  constexpr int TILEB = KVT * D;         // bytes of one K (or V^T) tile
+  constexpr int TILEB = KVT * D;         // bytes of one K (or V^T) tile in LDS
+  constexpr int MTILEB = PAIRED ? TILEB / 2 : TILEB;   // bytes of one K (or V^T) tile in memory
   constexpr int STAGE = 2 * TILEB;
   constexpr int KB = KVT / 32;           // copy steps per tile (one per 32-key block)
+  static_assert(!PAIRED || KVT == 128, "pairs of 64-key tiles make a 128-key LDS tile");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
   lds_u8* lds = (lds_u8*)smem;
 
@@ -122,8 +130,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   const int end = __builtin_amdgcn_readfirstlane(((cint*)p.qptr)[qrow_u + 1]);
   const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u]);
   cint* kv_idx = (cint*)p.kv_idx;
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (size_t)wi.bh * p.nK * TILEB;
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * TILEB;
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (size_t)wi.bh * p.nK * MTILEB;
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (size_t)wi.bh * p.nK * MTILEB;
   const float c2 = p.c2;
   const int km2 = (1 << p.lk2) - 1, km1 = (1 << p.lk1) - 1, ksh = p.lk1 + p.lk2;
   const int koff = dma_lane_offset<KROW, NW>(wv, lane);
@@ -133,12 +141,51 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   const int kswz = swz<KROW / 16>(krow0);
   const int vswz = swz<VROW / 16>(lq);
 
-  int kv_cur = kv_idx[beg];
-  int kv_nxt = beg + 1 < end ? kv_idx[beg + 1] : 0;
-  tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);
-  tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
-  const unsigned char* nk = kbase;
-  const unsigned char* nv = vbase;
+  // Copy of an LDS tile into the stage at nb, round by round; a round is
+  // 1024 * NW bytes and step kb of KB issues its share.  In a pair the K
+  // rounds of the first half come from tile ka, the rest from kb2; a V^T row
+  // takes its first 64 bytes from va and its last 64 from vb2.
+  constexpr int ROUND = 1024 * NW;
+  constexpr int ROUNDS = TILEB / ROUND;
+  const int vlc = (voff % VROW) / 16;                  // the lane's logical V^T chunk (same every round)
+  const int vrow0 = voff / VROW;
+  auto copy_step = [&](const unsigned char* ka, const unsigned char* va, const unsigned char* kb2,
+                       const unsigned char* vb2, lds_u8* nb, int kb) {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      if ((i * KB) / ROUNDS != kb) continue;
+      const unsigned char* ks;
+      const unsigned char* vs;
+      if constexpr (PAIRED) {
+        ks = (i < ROUNDS / 2 ? ka : kb2) + (i % (ROUNDS / 2)) * ROUND + koff;
+        const int r = vrow0 + i * (ROUND / VROW);
+        vs = (vlc < 4 ? va : vb2) + r * (VROW / 2) + (vlc & 3) * 16;
+      } else {
+        ks = ka + i * ROUND + koff;
+        vs = va + i * ROUND + voff;
+      }
+      __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(nb + i * ROUND + wv * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vs, (__attribute__((address_space(3))) void*)(nb + TILEB + i * ROUND + wv * 1024), 16, 0, 0);
+    }
+  };
+  constexpr int TSTEP = PAIRED ? 2 : 1;                // tile-map entries per LDS tile
+  // memory tiles of the LDS tile at entry j (a pair's second is its first
+  // again at the end of an odd row: valid memory whose keys the mask drops)
+  auto tile_ptrs = [&](int j, const unsigned char*& ka, const unsigned char*& va, const unsigned char*& kb2,
+                       const unsigned char*& vb2) {
+    const int c0 = kv_idx[j];
+    const int c1 = PAIRED && j + 1 < end ? kv_idx[j + 1] : c0;
+    ka = kbase + (size_t)c0 * MTILEB;
+    va = vbase + (size_t)c0 * MTILEB;
+    kb2 = kbase + (size_t)c1 * MTILEB;
+    vb2 = vbase + (size_t)c1 * MTILEB;
+  };
+  const unsigned char *nka, *nva, *nkb, *nvb;
+  tile_ptrs(beg, nka, nva, nkb, nvb);
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) copy_step(nka, nva, nkb, nvb, lds, kb);
   lds_u8* nbuf = lds;
 
   // S^T of 32-key block blk of the K tile at Ks
@@ -158,10 +205,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     constexpr bool BOUNDARY = decltype(bnd)::value;
 #pragma unroll 1
     for (int st = 0; st < NSTEP; ++st) {
-      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, 2 * st);
-      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, 2 * st);
-      tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, 2 * st + 1);
-      tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, 2 * st + 1);
+      copy_step(nka, nva, nkb, nvb, nbuf, 2 * st);
+      copy_step(nka, nva, nkb, nvb, nbuf, 2 * st + 1);
       f32x16 s0 = qk(Ks, 2 * st);
       f32x16 s1 = qk(Ks, 2 * st + 1);
       if constexpr (BOUNDARY) {
@@ -210,50 +255,62 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     }
   };
 
-  // Barrier for tile j and bookkeeping of the next tile's copy; returns the
-  // LDS buffers holding tile j.
+  // Barrier for the LDS tile at entry j and bookkeeping of the next one's
+  // copy; sets the LDS buffers holding it.
   auto begin_tile = [&](int j, const unsigned char*& Ks, const unsigned char*& Vs) {
-    const int stage = (j - beg) & 1;
+    const int stage = ((j - beg) / TSTEP) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
+    // the last LDS tile re-copies itself (into the idle buffer)
+    tile_ptrs(j + TSTEP < end ? j + TSTEP : j, nka, nva, nkb, nvb);
     nbuf = lds + (stage ^ 1) * STAGE;
-    nk = kbase + (size_t)kv_copy * TILEB;
-    nv = vbase + (size_t)kv_copy * TILEB;
-    const int kv = kv_cur;
-    kv_cur = kv_nxt;
-    if (j + 2 < end) kv_nxt = kv_idx[j + 2];
     Ks = smem + stage * STAGE;
     Vs = Ks + TILEB;
-    return kv;
+  };
+  // validity mask of this lane's query over KV tile kv: NG groups of 8 keys,
+  // group gg at tile slot slot0(gg), placed at bit 8 (gg + g0)
+  auto kv_tile_mask = [&](int kv, auto ng, auto slot0) {
+    constexpr int NG = decltype(ng)::value;
+    const int k2 = (kv % p.nk2) << p.lk2;
+    const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+    const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+    return boundary_mask<NG>(slot0, k0, k1, k2, st0, st1, st2, p.w0, p.w1, p.w2, p.lk2, km1, km2, ksh);
+  };
+  // validity mask of the LDS tile at entry j (group gg holds keys
+  // 32 (gg / 2) + 16 hh + 8 (gg % 2) .. + 7 of the LDS tile)
+  auto lds_tile_mask = [&](int j) {
+    if constexpr (PAIRED) {
+      // groups 0..3 are keys 0..63 (the first tile), 4..7 keys 64..127 (the second)
+      auto slot = [&](int gg) { return 32 * (gg >> 1) + 16 * hh + 8 * (gg & 1); };
+      const uint64_t ma = kv_tile_mask(kv_idx[j], std::integral_constant<int, 4>{}, slot);
+      const uint64_t mb = j + 1 < end ? kv_tile_mask(kv_idx[j + 1], std::integral_constant<int, 4>{}, slot) : 0ull;
+      return ma | (mb << 32);
+    } else {
+      return kv_tile_mask(kv_idx[j], std::integral_constant<int, KVT / 16>{},
+                          [&](int gg) { return 32 * (gg >> 1) + 16 * hh + 8 * (gg & 1); });
+    }
   };
 
   // Three homogeneous loops (padding-only waves copy; full tiles; boundary
   // tiles), so the accumulators flow through simple loop phis.
   const unsigned char* Ks;
   const unsigned char* Vs;
+  // LDS tiles before jfull have only full tile-map entries
+  const int jfull = beg + (nfull / TSTEP) * TSTEP;
   if (!wave_active) {
-    for (int j = beg; j < end; ++j) {
+    for (int j = beg; j < end; j += TSTEP) {
       begin_tile(j, Ks, Vs);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        tile_to_lds_step<TILEB, NW, KB>(nk, koff, nbuf, wv, kb);
-        tile_to_lds_step<TILEB, NW, KB>(nv, voff, nbuf + TILEB, wv, kb);
-      }
+      for (int kb = 0; kb < KB; ++kb) copy_step(nka, nva, nkb, nvb, nbuf, kb);
     }
   } else {
-    for (int j = beg; j < beg + nfull; ++j) {
+    for (int j = beg; j < jfull; j += TSTEP) {
       begin_tile(j, Ks, Vs);
       tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
     }
-    for (int j = beg + nfull; j < end; ++j) {
-      const int kv = begin_tile(j, Ks, Vs);
-      const int k2 = (kv % p.nk2) << p.lk2;
-      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
-      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
-      const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 32 * (gg >> 1) + 16 * hh + 8 * (gg & 1); }, k0, k1, k2, st0, st1, st2, p.w0,
-                                                     p.w1, p.w2, p.lk2, km1, km2, ksh);
-      tile_body(Ks, Vs, vmask, std::integral_constant<bool, true>{});
+    for (int j = jfull; j < end; j += TSTEP) {
+      begin_tile(j, Ks, Vs);
+      tile_body(Ks, Vs, lds_tile_mask(j), std::integral_constant<bool, true>{});
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -280,12 +337,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
         m == -INFINITY ? 0.f : m * p.scale + logf(lt) - kPScaleLog2 * 0.69314718055994531f;
 }
 
+// 64-key KV tiles run as pairs in the 128-key LDS tile
 template <int NW, int KVT>
 hipError_t launch_cfg(const KParams& p, int io, hipStream_t st) {
+  constexpr bool PAIRED = KVT == 64;
+  constexpr int LKVT = PAIRED ? 128 : KVT;
   if (io == IO_QO)
-    attn_fp8_kernel<128, NW, KVT, true><<<p.num_wg, NW * 64, 0, st>>>(p);
+    attn_fp8_kernel<128, NW, LKVT, true, PAIRED><<<p.num_wg, NW * 64, 0, st>>>(p);
   else
-    attn_fp8_kernel<128, NW, KVT, false><<<p.num_wg, NW * 64, 0, st>>>(p);
+    attn_fp8_kernel<128, NW, LKVT, false, PAIRED><<<p.num_wg, NW * 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
