@@ -201,57 +201,84 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     return s;
   };
 
+  // lazy rescaling on the 64 keys (s0, s1) of one step: the reference max
+  // moves only when their max exceeds it by 2^2 (after exp2)
+  auto rescale = [&](const f32x16& s0, const f32x16& s1) {
+    // one serial chain of three-input maxima (v_max3_f32)
+    float bm = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
+#pragma unroll
+    for (int i = 1; i < 15; ++i) bm = fmaxf(fmaxf(bm, s1[i]), s0[i + 1]);
+    bm = fmaxf(bm, s1[15]);
+    bm = xhalf_max(bm);
+    if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {   // rare after the first steps
+      const float mn = fmaxf(m, bm);
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
+#pragma unroll
+      for (int d = 0; d < DB; ++d) o[d] *= alpha;
+      osum *= alpha;
+      m = mn;
+    }
+  };
+
+  // P = e4m3(64 exp2(S c2 - m c2)) of step st and O^T += V^T P^T over its 64
+  // keys, with the row sums through an all-ones A
+  auto softmax_pv = [&](const f32x16& s0, const f32x16& s1, const unsigned char* Vs, int st) {
+    // P bytes: byte j < 16 is key 16 hh + j of block 2 st, byte 16 + j key 16 hh + j of block 2 st + 1
+    const float nref = (m == -INFINITY ? 0.f : -m * c2) + kPScaleLog2;
+    i32x8 pb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q], c2, nref)),
+                                               __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 1], c2, nref)), 0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q + 2], c2, nref)),
+                                           __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 3], c2, nref)), w0, true);
+      int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q], c2, nref)),
+                                               __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 1], c2, nref)), 0, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q + 2], c2, nref)),
+                                           __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 3], c2, nref)), w1, true);
+      pb[q] = w0;
+      pb[4 + q] = w1;
+    }
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      const unsigned char* vr = Vs + (d * 32 + lq) * VROW;
+      const int c0 = 4 * st + hh, c1 = 4 * st + 2 + hh;
+      const i32x8 a = gload32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
+      o[d] = mfma8(a, pb, o[d]);
+    }
+    osum = mfma8(ones, pb, osum);
+  };
+
+  // One LDS tile: a software pipeline over its 64-key steps -- S^T of step
+  // st + 1 is issued before the exponentials of step st, so the wave has
+  // matrix work beside them.
   auto tile_body = [&](const unsigned char* Ks, const unsigned char* Vs, uint64_t vmask, auto bnd) {
     constexpr bool BOUNDARY = decltype(bnd)::value;
-#pragma unroll 1
+    f32x16 s0 = qk(Ks, 0), s1 = qk(Ks, 1);
+    if constexpr (BOUNDARY) {
+      apply_mask(s0, vmask, 0);
+      apply_mask(s1, vmask, 1);
+    }
+    rescale(s0, s1);
+#pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       copy_step(nka, nva, nkb, nvb, nbuf, 2 * st);
       copy_step(nka, nva, nkb, nvb, nbuf, 2 * st + 1);
-      f32x16 s0 = qk(Ks, 2 * st);
-      f32x16 s1 = qk(Ks, 2 * st + 1);
-      if constexpr (BOUNDARY) {
-        apply_mask(s0, vmask, 2 * st);
-        apply_mask(s1, vmask, 2 * st + 1);
+      f32x16 t0, t1;
+      if (st + 1 < NSTEP) {
+        t0 = qk(Ks, 2 * st + 2);
+        t1 = qk(Ks, 2 * st + 3);
       }
-      // one serial chain of three-input maxima (v_max3_f32)
-      float bm = fmaxf(fmaxf(s0[0], s1[0]), s0[1]);
-#pragma unroll
-      for (int i = 1; i < 15; ++i) bm = fmaxf(fmaxf(bm, s1[i]), s0[i + 1]);
-      bm = fmaxf(bm, s1[15]);
-      bm = xhalf_max(bm);
-      if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {   // lazy rescaling, rare after the first steps
-        const float mn = fmaxf(m, bm);
-        const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
-#pragma unroll
-        for (int d = 0; d < DB; ++d) o[d] *= alpha;
-        osum *= alpha;
-        m = mn;
+      softmax_pv(s0, s1, Vs, st);
+      if (st + 1 < NSTEP) {
+        if constexpr (BOUNDARY) {
+          apply_mask(t0, vmask, 2 * st + 2);
+          apply_mask(t1, vmask, 2 * st + 3);
+        }
+        rescale(t0, t1);
+        s0 = t0;
+        s1 = t1;
       }
-      // P bytes: byte j < 16 is key 16 hh + j of block 2 st, byte 16 + j key 16 hh + j of block 2 st + 1
-      const float nref = (m == -INFINITY ? 0.f : -m * c2) + kPScaleLog2;
-      i32x8 pb;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q], c2, nref)),
-                                                 __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 1], c2, nref)), 0, false);
-        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q + 2], c2, nref)),
-                                             __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 3], c2, nref)), w0, true);
-        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q], c2, nref)),
-                                                 __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 1], c2, nref)), 0, false);
-        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q + 2], c2, nref)),
-                                             __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 3], c2, nref)), w1, true);
-        pb[q] = w0;
-        pb[4 + q] = w1;
-      }
-      // O^T += V^T P^T (64 keys), and the row sums through an all-ones A
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const unsigned char* vr = Vs + (d * 32 + lq) * VROW;
-        const int c0 = 4 * st + hh, c1 = 4 * st + 2 + hh;
-        const i32x8 a = gload32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
-        o[d] = mfma8(a, pb, o[d]);
-      }
-      osum = mfma8(ones, pb, osum);
     }
   };
 
