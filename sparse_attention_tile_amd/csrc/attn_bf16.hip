@@ -93,17 +93,26 @@ __device__ __forceinline__ void tile_to_lds_step_off(const unsigned char* __rest
                                        0);
 }
 
-template <int D, int NW, int KVT, int IO>
+// PAIRED (k, v in tile order, 8 waves): the KV tiles in memory hold 64 keys
+// and two consecutive entries of a tile-map row are copied into one 128-key
+// LDS tile (K rows 0..63 from the first, 64..127 from the second; each V^T
+// row's first and second halves likewise), so the 128-key pipeline runs with
+// one barrier per 128 keys.  A pair is full when both of its tiles are; an
+// odd row ends with a single tile whose second half is masked.
+template <int D, int NW, int KVT, int IO, bool PAIRED>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   constexpr bool GQ = IO != IO_TILE;     // q, out, lse in grid order
   constexpr bool GKV = IO == IO_GRID;    // k, v in grid order
+  static_assert(!PAIRED || (KVT == 128 && !GKV), "pairs of 64-key tiles in tile order make a 128-key LDS tile");
   constexpr int QT = NW * 32;            // queries per workgroup
   constexpr int DC = D / 16;             // k-steps of S^T
   constexpr int DB = D / 32;             // 32-row blocks of O^T
   constexpr int KB = KVT / 32;           // 32-key blocks per KV tile
   constexpr int KROW = D * 2;            // bytes per K row
   constexpr int VROW = GKV ? D * 2 : KVT * 2;    // bytes per V row (GKV) or V^T row
-  constexpr int TILEB = KVT * D * 2;     // bytes of one K (or V) tile
+  constexpr int TILEB = KVT * D * 2;     // bytes of one K (or V) tile in LDS
+  constexpr int MTILEB = PAIRED ? TILEB / 2 : TILEB;   // bytes of one K (or V^T) tile in memory
+  constexpr int TSTEP = PAIRED ? 2 : 1;  // tile-map entries per LDS tile
   constexpr int ROUNDS = TILEB / (1024 * NW);    // copy rounds per tile
   constexpr int STAGE = 2 * TILEB;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
@@ -169,8 +178,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   const int beg = __builtin_amdgcn_readfirstlane(qptr[qrow_u]) + kvo;
   const int end = __builtin_amdgcn_readfirstlane(qptr[qrow_u + 1]) + kvo;
   const int nfull = __builtin_amdgcn_readfirstlane(((cint*)p.n_full)[qrow_u + bh_u * p.map_bh_nf]);
-  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
-  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * TILEB);
+  const unsigned char* kbase = static_cast<const unsigned char*>(p.kt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * MTILEB);
+  const unsigned char* vbase = static_cast<const unsigned char*>(p.vt) + (GKV ? grid_base * 2 : (size_t)wi.bh * p.nK * MTILEB);
   const float c2 = p.c2;
   const int km2 = (1 << p.lk2) - 1, km1 = (1 << p.lk1) - 1, ksh = p.lk1 + p.lk2;
   static_assert(KVT / 16 <= 8, "validity mask holds 64 bits");
@@ -213,12 +222,48 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   // sits between a barrier and the next tile's DMA.
   int kv_cur = kv_idx[beg];
   int kv_nxt = beg + 1 < end ? kv_idx[beg + 1] : 0;
+  // PAIRED: memory tiles of the pair being copied (nka, nva, nkb, nvb) and
+  // the entries of the pair after it, fetched one pair ahead (pc0, pc1; an
+  // odd row's last pair repeats its first tile, whose copy the mask drops)
+  const unsigned char *nka = kbase, *nva = vbase, *nkb = kbase, *nvb = vbase;
+  int pc0 = 0, pc1 = 0;
+  if constexpr (PAIRED) {
+    const int c1 = beg + 1 < end ? kv_nxt : kv_cur;
+    nka = kbase + (size_t)kv_cur * MTILEB;
+    nva = vbase + (size_t)kv_cur * MTILEB;
+    nkb = kbase + (size_t)c1 * MTILEB;
+    nvb = vbase + (size_t)c1 * MTILEB;
+    pc0 = beg + 2 < end ? kv_idx[beg + 2] : kv_cur;
+    pc1 = beg + 3 < end ? kv_idx[beg + 3] : pc0;
+  }
+  // PAIRED copy step kb: K rounds of the first half from tile a, the rest
+  // from tile b; a V^T row's first VROW / 2 bytes from a, the rest from b
+  const int vlc = (voff % VROW) / 16;    // the lane's logical V^T chunk (same every round)
+  const int vrow0 = voff / VROW;
+  auto pair_copy_step = [&](lds_u8* nb, int kb) {
+    constexpr int ROUND = 1024 * NW;
+    constexpr int HALF = VROW / 32;      // chunks per half V^T row
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      if ((i * KB) / ROUNDS != kb) continue;
+      const unsigned char* ks = (i < ROUNDS / 2 ? nka : nkb) + (i % (ROUNDS / 2)) * ROUND + koff;
+      const int r = vrow0 + i * (ROUND / VROW);
+      const unsigned char* vs = (vlc < HALF ? nva : nvb) + r * (VROW / 2) + (vlc % HALF) * 16;
+      __builtin_amdgcn_global_load_lds(ks, (__attribute__((address_space(3))) void*)(nb + i * ROUND + wv * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(
+          vs, (__attribute__((address_space(3))) void*)(nb + TILEB + i * ROUND + wv * 1024), 16, 0, 0);
+    }
+  };
   if constexpr (GKV) {    // prologue: tile 0 in flight
     grid_offsets(kv_cur);
     for (int kb = 0; kb < KB; ++kb) {
       tile_to_lds_step_off<TILEB, NW, KB>(kbase, goff, lds, wv, kb);
       tile_to_lds_step_off<TILEB, NW, KB>(vbase, goff, lds + TILEB, wv, kb);
     }
+  } else if constexpr (PAIRED) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) pair_copy_step(lds, kb);
   } else {
     tile_to_lds<TILEB, NW>(kbase + (size_t)kv_cur * TILEB, koff, lds, wv);
     tile_to_lds<TILEB, NW>(vbase + (size_t)kv_cur * TILEB, voff, lds + TILEB, wv);
@@ -237,6 +282,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
     if constexpr (GKV) {
       tile_to_lds_step_off<TILEB, NW, KB>(kbase, goff, nb, wv, kb);
       tile_to_lds_step_off<TILEB, NW, KB>(vbase, goff, nb + TILEB, wv, kb);
+    } else if constexpr (PAIRED) {
+      pair_copy_step(nb, kb);
     } else {
       tile_to_lds_step<TILEB, NW, KB>(nk, koff, nb, wv, kb);
       tile_to_lds_step<TILEB, NW, KB>(nv, voff, nb + TILEB, wv, kb);
@@ -299,47 +346,73 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   // Barrier for tile j and bookkeeping of the next tile's copy; returns the
   // LDS buffers holding tile j.
   auto begin_tile = [&](int j, const unsigned char*& Ks, const unsigned char*& Vs) {
-    const int stage = (j - beg) & 1;
+    const int stage = ((j - beg) / TSTEP) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
     nbuf = lds + (stage ^ 1) * STAGE;
-    if constexpr (GKV) {
-      grid_offsets(kv_copy);
+    int kv = kv_cur;
+    if constexpr (PAIRED) {
+      if (j + 2 < end) {                 // else the last pair re-copies itself (idle buffer)
+        nka = kbase + (size_t)pc0 * MTILEB;
+        nva = vbase + (size_t)pc0 * MTILEB;
+        nkb = kbase + (size_t)pc1 * MTILEB;
+        nvb = vbase + (size_t)pc1 * MTILEB;
+        pc0 = j + 4 < end ? kv_idx[j + 4] : pc0;
+        pc1 = j + 5 < end ? kv_idx[j + 5] : pc0;
+      }
     } else {
-      nk = kbase + (size_t)kv_copy * TILEB;
-      nv = vbase + (size_t)kv_copy * TILEB;
+      const int kv_copy = j + 1 < end ? kv_nxt : kv_cur;   // the last tile re-copies itself (idle buffer)
+      if constexpr (GKV) {
+        grid_offsets(kv_copy);
+      } else {
+        nk = kbase + (size_t)kv_copy * TILEB;
+        nv = vbase + (size_t)kv_copy * TILEB;
+      }
+      kv_cur = kv_nxt;
+      if (j + 2 < end) kv_nxt = kv_idx[j + 2];
     }
-    const int kv = kv_cur;
-    kv_cur = kv_nxt;
-    if (j + 2 < end) kv_nxt = kv_idx[j + 2];
     Ks = smem + stage * STAGE;
     Vs = Ks + TILEB;
     return kv;
+  };
+  // validity mask of this lane's query over NG groups of KV tile kv (group
+  // gg: keys 16 gg + 8 hh .. + 7 of the tile)
+  auto kv_tile_mask = [&](int kv, auto ng) {
+    constexpr int NG = decltype(ng)::value;
+    const int k2 = (kv % p.nk2) << p.lk2;
+    const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+    const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+    return boundary_mask<NG>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1, st2, p.w0, p.w1, p.w2,
+                             p.lk2, km1, km2, ksh);
   };
 
   // Three homogeneous loops (padding-only waves copy; full tiles; boundary
   // tiles), so the accumulators flow through simple loop phis.
   const unsigned char* Ks;
   const unsigned char* Vs;
+  // LDS tiles before jfull have only full tile-map entries
+  const int jfull = beg + (nfull / TSTEP) * TSTEP;
   if (!wave_active) {
-    for (int j = beg; j < end; ++j) {
+    for (int j = beg; j < end; j += TSTEP) {
       begin_tile(j, Ks, Vs);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) copy_step(nbuf, kb);
     }
   } else {
-    for (int j = beg; j < beg + nfull; ++j) {
+    for (int j = beg; j < jfull; j += TSTEP) {
       begin_tile(j, Ks, Vs);
       tile_body(Ks, Vs, nbuf, 0ull, std::integral_constant<bool, false>{});
     }
-    for (int j = beg + nfull; j < end; ++j) {
+    for (int j = jfull; j < end; j += TSTEP) {
       const int kv = begin_tile(j, Ks, Vs);
-      const int k2 = (kv % p.nk2) << p.lk2;
-      const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
-      const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
-      const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1, st2, p.w0,
-                                                     p.w1, p.w2, p.lk2, km1, km2, ksh);
+      uint64_t vmask;
+      if constexpr (PAIRED) {   // the two tiles' masks side by side (groups 0..3, 4..7)
+        const uint64_t ma = kv_tile_mask(kv_idx[j], std::integral_constant<int, 4>{});
+        const uint64_t mb = j + 1 < end ? kv_tile_mask(kv_idx[j + 1], std::integral_constant<int, 4>{}) : 0ull;
+        vmask = ma | (mb << 32);
+      } else {
+        vmask = kv_tile_mask(kv, std::integral_constant<int, KVT / 16>{});
+      }
       tile_body(Ks, Vs, nbuf, vmask, std::integral_constant<bool, true>{});
     }
   }
@@ -369,14 +442,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
         (m == -INFINITY ? 0.f : m * p.scale) + logf(lt);
 }
 
+// 8-wave workgroups run 64-key tiles in tile order as pairs in a 128-key
+// LDS tile (4-wave ones keep 64-key stages: two such workgroups share a CU)
 template <int D, int NW, int KVT>
 hipError_t launch_cfg(const KParams& p, int io, hipStream_t st) {
+  constexpr bool PAIRED = KVT == 64 && NW == 8;
+  constexpr int LKVT = PAIRED ? 128 : KVT;
   if (io == IO_GRID)
-    attn_bf16_kernel<D, NW, KVT, IO_GRID><<<p.num_wg, NW * 64, 0, st>>>(p);
+    attn_bf16_kernel<D, NW, KVT, IO_GRID, false><<<p.num_wg, NW * 64, 0, st>>>(p);
   else if (io == IO_QO)
-    attn_bf16_kernel<D, NW, KVT, IO_QO><<<p.num_wg, NW * 64, 0, st>>>(p);
+    attn_bf16_kernel<D, NW, LKVT, IO_QO, PAIRED><<<p.num_wg, NW * 64, 0, st>>>(p);
   else
-    attn_bf16_kernel<D, NW, KVT, IO_TILE><<<p.num_wg, NW * 64, 0, st>>>(p);
+    attn_bf16_kernel<D, NW, LKVT, IO_TILE, PAIRED><<<p.num_wg, NW * 64, 0, st>>>(p);
   return hipGetLastError();
 }
 
