@@ -41,7 +41,10 @@
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null
  * stream).  Device entry points only enqueue work: they return before it
- * runs and do not synchronise.
+ * runs and do not synchronise.  The first na_forward / na_backward call
+ * for a geometry builds its plan (host tile map, allocated and uploaded
+ * synchronously); after that these calls only launch kernels, so they can
+ * be captured in a HIP graph (tested: every replay equals the eager call).
  *
  * Empty problems.  batch == 0 or heads == 0 is valid: device entry points
  * then launch nothing and return NA_OK (pointers are not checked).

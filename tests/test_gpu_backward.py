@@ -141,3 +141,39 @@ def test_dkdv_split_equals_fused_full_size(na, monkeypatch):
     b = _run(na, wl, q, k, v, do)
     for x, y in zip(a[2:], b[2:]):
         assert torch.equal(x, y)
+
+
+def test_backward_replays_in_a_hip_graph(na):
+    # na_backward enqueues kernels only once the plan (and its transposed map)
+    # exists, so it can be captured; every replay equals the eager gradients
+    wl = WORKLOADS["video_sliding"].with_(batch=1, heads=2, grid=(5, 19, 27), window=(3, 7, 9), stride=(1, 2, 3),
+                                          seed=81)
+    qc, kc, vc, _ = make_qkv(wl, device="cpu")
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+    do = _dout(wl, 82).cuda()
+    out, lse, dq_e, dk_e, dv_e = _run(na, wl, q, k, v, do)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    nb = na.na_backward_workspace_bytes(B, H, D, wl.grid, wl.window, wl.stride, na.NA_BF16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    grads = [torch.empty_like(q) for _ in range(3)]
+    say("[bwd] graph replay")
+
+    def call():
+        na.na_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                       grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), B, H, D, wl.grid, wl.window,
+                       wl.stride, wl.scale, na.NA_BF16, ws.data_ptr(), nb,
+                       torch.cuda.current_stream().cuda_stream)
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        for t in grads:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, e in zip(grads, (dq_e, dk_e, dv_e)):
+            assert torch.equal(t, e)

@@ -255,3 +255,27 @@ def test_offsets_beyond_32_bits_match_the_small_problem(na, path):
         assert torch.equal(lb[b, ..., h], lse[0, ..., h % wl.heads]), (b, h)
     del fb, qb, kb, vb, ob, lb
     torch.cuda.empty_cache()
+
+
+def test_forward_replays_in_a_hip_graph(na, path):
+    # After a first call has built the plan, na_forward only enqueues kernels,
+    # so it can be captured in a HIP graph.  Each replay must equal the eager
+    # result bit for bit; the outputs are poisoned by eager work in between.
+    import gpu_util
+    wl = WORKLOADS["video_block"].with_(grid=(8, 16, 24), window=(6, 8, 8), stride=(4, 4, 4), heads=2, seed=311)
+    say(f"[special] graph replay ({path})")
+    _, _, _, _, q, k, v = inputs(wl)
+    f = na.Forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=gpu_util.USE_WORKSPACE)
+    out_e, lse_e = f()
+    torch.cuda.synchronize()
+    out_e, lse_e = out_e.clone(), lse_e.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        f()
+    for _ in range(3):
+        f.out.fill_(float("nan"))
+        f.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(f.out, out_e) and torch.equal(f.lse, lse_e)
