@@ -31,13 +31,14 @@ def _ref_tile_order(x, tile, transpose):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32, torch.float8_e4m3fn])
 @pytest.mark.parametrize("tile", [(2, 8, 8), (1, 4, 16), (4, 2, 2)])
 @pytest.mark.parametrize("transpose", [False, True])
-def test_permute_layout_and_round_trip(na, dtype, tile, transpose):
+@pytest.mark.parametrize("heads", [3, 11])   # 11: head groups of 8, the last one partial
+def test_permute_layout_and_round_trip(na, dtype, tile, transpose, heads):
     if transpose and dtype == torch.float32:
         pytest.skip("fp32 path keeps V untransposed")
     D = 64 if dtype != torch.float8_e4m3fn else 128
-    say(f"[permute] {dtype} tile={tile} transpose={transpose}")
+    say(f"[permute] {dtype} tile={tile} transpose={transpose} heads={heads}")
     g = torch.Generator("cpu").manual_seed(5)
-    x = torch.randn((2, 5, 11, 13, 3, D), generator=g).to(dtype)
+    x = torch.randn((2, 5, 11, 13, heads, D), generator=g).to(dtype)
     xg = x.cuda()
     xt = na.permute(xg, tile, transpose=transpose)
     torch.cuda.synchronize()
