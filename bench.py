@@ -156,7 +156,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_block",
                     help="video_block (default), video_sliding, img256_block, img256_block_fp8, img64_sliding, "
-                         "img64_block, img16_f32")
+                         "img64_block, img16_f32, video_dense")
     ap.add_argument("--head-dim", type=int, default=None,
                     help="run the workload's geometry at another head_dim (synthetic inputs of that shape)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
