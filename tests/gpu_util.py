@@ -11,11 +11,14 @@ import oracle
 from synth import make_qkv, to_f64
 
 # max-abs tolerances on N(0,1) inputs.  out: the workload specification's
-# bounds.  lse: fp32 / bf16 from the fp32 softmax statistics and v_exp_f32
-# rounding; fp8 from the e4m3 quantisation of P: l sums weights that each carry
-# a relative rounding error of at most 2^-4 (3 mantissa bits), so
-# |d lse| <= ln(1 + 2^-4) = 0.0606.
-TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, 2e-3), "fp8": (6e-2, 6.1e-2)}
+# bounds.  lse: l sums the weights exactly as the PV product uses them,
+# rounded to the product's type (bf16: 8 significant bits, relative error at
+# most 2^-8 each; e4m3: 4 bits, 2^-4), so |d lse| <= ln(1 + 2^-8) = 3.90e-3 for
+# bf16 and ln(1 + 2^-4) = 0.0606 for fp8, plus fp32 rounding of the
+# statistics (2e-5 / 1e-4 of slack); fp32 from its fp32 statistics alone.
+# Large windows average the rounding out (measured ~1e-3 for bf16); windows of
+# a few keys can approach the bound.
+TOL = {"f32": (1e-5, 1e-4), "bf16": (2e-2, math.log1p(2.0 ** -8) + 2e-5), "fp8": (6e-2, 6.1e-2)}
 
 
 def say(*a):

@@ -280,3 +280,29 @@ def test_forward_replays_in_a_hip_graph(na, path):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(f.out, out_e) and torch.equal(f.lse, lse_e)
+
+
+@pytest.mark.parametrize("grid", [(1, 1, 1), (1, 1, 5), (1, 3, 1), (2, 1, 1), (3, 2, 1), (1, 1, 9)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "fp8"])
+def test_tiny_grids(na, path, grid, dtype):
+    # grids of one to nine tokens: tiles mostly padding, every query sees
+    # every token (window = grid)
+    if path != "qo" and dtype != "bf16":
+        pytest.skip("the other forms are bf16 only")
+    base = {"bf16": WORKLOADS["img64_block"], "f32": WORKLOADS["img16_f32"], "fp8": WORKLOADS["img256_block_fp8"]}[dtype]
+    wl = base.with_(batch=2, heads=3, grid=grid, window=grid, stride=(1, 1, 1), seed=400 + sum(grid))
+    say(f"[special] tiny grid {grid} {dtype} ({path})")
+    qc, kc, vc, sc, q, k, v = inputs(wl)
+    out, lse, _ = run_hip(na, wl, q, k, v, sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    to, tl = TOL[wl.dtype]
+    if dtype != "f32":
+        # A few keys do not average the rounding of the weights out: each
+        # weight carries a relative error of at most u (bf16 2^-8, e4m3 2^-4)
+        # before normalisation, so the normalised weights move by at most
+        # 2u / (1 - u) in total and out by that times max |v| (vc holds the
+        # values exactly as both sides use them, before the v dequantisation).
+        u = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -4
+        vmax = float(vc.float().abs().max()) * sc[2]
+        to = max(to, 2 * u / (1 - u) * vmax)
+    assert eo <= to and el <= tl
