@@ -58,8 +58,11 @@ __device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, flo
 #pragma unroll
   for (int i = 3; i < 15; i += 2) bm = fmaxf(fmaxf(bm, s[i]), s[i + 1]);
   bm = fmaxf(bm, s[15]);
-  bm = xhalf_max(bm);
+  // m is the same in both lane halves (one query), so testing each half's
+  // maximum decides the branch as the full row maximum would; the exchange
+  // between the halves is only needed inside it
   if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {
+    bm = xhalf_max(bm);
     const float mn = fmaxf(m, bm);
     // alpha = 0 while nothing was accumulated (O and l are still 0)
     const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);

@@ -209,8 +209,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
 #pragma unroll
     for (int i = 1; i < 15; ++i) bm = fmaxf(fmaxf(bm, s1[i]), s0[i + 1]);
     bm = fmaxf(bm, s1[15]);
-    bm = xhalf_max(bm);
+    // each lane half tests its own maximum (m is shared by the halves); the
+    // full row maximum is formed only when the branch is taken
     if (__builtin_amdgcn_ballot_w64(bm > m + thr)) {   // rare after the first steps
+      bm = xhalf_max(bm);
       const float mn = fmaxf(m, bm);
       const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mn) * c2);
 #pragma unroll
