@@ -20,8 +20,16 @@
 //   32 P bytes its PV B operand needs, straight from registers.
 // * P is stored as e4m3(64 p): the lazy-rescaling threshold is 2^2 here, so
 //   64 p <= 256 stays inside e4m3's range (448) while small weights keep
-//   precision.  l is computed by the matrix core from the same quantised P
-//   (an all-ones A operand), so O / l cancels the factor 64 exactly.
+//   precision.  l is computed by the matrix core from the same quantised P,
+//   so O / l cancels the factor 64 exactly: a 16x16x128 product whose A
+//   operand is e4m3 1.0 in the lane groups that hold the keys of the output
+//   row's query and 0 elsewhere (output row r of lane group g belongs to
+//   query 16 (r / 4 % 2) + column, and lane groups g and g + 2 hold the two
+//   key halves of one query), so every output element of a lane is its
+//   query's row sum.
+// * The first conversion into each P dword takes that dword's previous
+//   contents as the bytes it keeps (the second conversion overwrites them),
+//   which saves zeroing it first.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -119,10 +127,14 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   f32x16 o[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
-  f32x16 osum = f32x16{};                 // every row: sum of the stored P of this lane's query
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  f32x4_t osum = {};                      // every element: sum of the stored P of this lane's query
   float m = -INFINITY;
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+  // A operand of the row-sum product (16x16x128): e4m3 1.0 where the lane
+  // group holds the keys of the query this output row belongs to, else 0
+  const int selv = (((lane >> 2) ^ (lane >> 4)) & 1) ? 0 : 0x38383838;
+  const i32x8 sel = {selv, selv, selv, selv, selv, selv, selv, selv};
+  i32x8 pb = {};
 
   typedef const __attribute__((address_space(4))) int32_t cint;
   const int qrow_u = __builtin_amdgcn_readfirstlane(wi.qrow);
@@ -223,19 +235,18 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   };
 
   // P = e4m3(64 exp2(S c2 - m c2)) of step st and O^T += V^T P^T over its 64
-  // keys, with the row sums through an all-ones A
+  // keys, with the row sums through the selector product
   auto softmax_pv = [&](const f32x16& s0, const f32x16& s1, const unsigned char* Vs, int st) {
     // P bytes: byte j < 16 is key 16 hh + j of block 2 st, byte 16 + j key 16 hh + j of block 2 st + 1
     const float nref = (m == -INFINITY ? 0.f : -m * c2) + kPScaleLog2;
-    i32x8 pb;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q], c2, nref)),
-                                               __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 1], c2, nref)), 0, false);
+                                               __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 1], c2, nref)), pb[q], false);
       w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q + 2], c2, nref)),
                                            __builtin_amdgcn_exp2f(fmaf(s0[4 * q + 3], c2, nref)), w0, true);
       int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q], c2, nref)),
-                                               __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 1], c2, nref)), 0, false);
+                                               __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 1], c2, nref)), pb[4 + q], false);
       w1 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s1[4 * q + 2], c2, nref)),
                                            __builtin_amdgcn_exp2f(fmaf(s1[4 * q + 3], c2, nref)), w1, true);
       pb[q] = w0;
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
       const i32x8 a = gload32(vr + ((c0 ^ vswz) * 16), vr + ((c1 ^ vswz) * 16));
       o[d] = mfma8(a, pb, o[d]);
     }
-    osum = mfma8(ones, pb, osum);
+    osum = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, pb, osum, 0, 0, 0, 127, 0, 127);
   };
 
   // One LDS tile: a software pipeline over its 64-key steps -- S^T of step
