@@ -141,16 +141,27 @@ na_status get_plan_t(const na::Geometry& g, const int tq[3], const int tkv[3], P
   if (st != NA_OK) return st;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!p->has_t) {
+    // a failed attempt leaves no device memory behind (the next call retries)
+    auto drop = [&]() {
+      for (int32_t** q : {&p->d_tptr, &p->d_tidx, &p->d_tnfull}) {
+        if (*q) (void)hipFree(*q);
+        *q = nullptr;
+      }
+    };
     const na::TransposedMap t = na::transpose_tile_map(p->map);
     const size_t nk = t.n_full.size(), nnz = t.q_idx.size();
     if (hipMalloc(&p->d_tptr, (nk + 1) * sizeof(int32_t)) != hipSuccess ||
         hipMalloc(&p->d_tidx, (nnz ? nnz : 1) * sizeof(int32_t)) != hipSuccess ||
-        hipMalloc(&p->d_tnfull, (nk ? nk : 1) * sizeof(int32_t)) != hipSuccess)
+        hipMalloc(&p->d_tnfull, (nk ? nk : 1) * sizeof(int32_t)) != hipSuccess) {
+      drop();
       return fail(NA_ERR_HIP, "hipMalloc of the transposed tile map failed");
+    }
     if (hipMemcpy(p->d_tptr, t.kptr.data(), (nk + 1) * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess ||
         (nnz && hipMemcpy(p->d_tidx, t.q_idx.data(), nnz * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess) ||
-        (nk && hipMemcpy(p->d_tnfull, t.n_full.data(), nk * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess))
+        (nk && hipMemcpy(p->d_tnfull, t.n_full.data(), nk * sizeof(int32_t), hipMemcpyHostToDevice) != hipSuccess)) {
+      drop();
       return fail(NA_ERR_HIP, "upload of the transposed tile map failed");
+    }
     p->has_t = true;
   }
   *out = p;
