@@ -273,16 +273,16 @@ bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tk
 // workgroup of w waves gets at most w / 8 of it.  Workgroups are dealt in
 // rounds of 256 x slots; the time is rounds x one workgroup's average time,
 // plus a launch overhead.  Calibration (one MI355X, kernel ms measured with
-// HIP events):
-//   bf16 D 128: 1.11e15 FLOP/s on full tiles (91 %-sparse video, 14.1 ms);
-//   boundary tiles 1.2x (video sliding window, 23.5 % boundary, 77.7 ms);
-//   fp8 D 128: 1.46e15 (4K image, 2.26 ms); launch 15 us (64x64 image, 43 us);
-//   fp32: 4.3e13 (16x16 image); bf16 D 64: 0.90e15 (the video block problem
-//   at head_dim 64, 8.66 ms).
+// HIP events; boxes differ by a few per cent):
+//   bf16 D 128: 1.15e15 FLOP/s of computed work on full tiles (91 %-sparse
+//   video, 13.0-13.5 ms); boundary tiles 1.2x (video sliding window, 23.5 %
+//   boundary, 74-75 ms); fp8 D 128: 1.79e15 (4K image, 1.94-1.99 ms); launch
+//   15 us (64x64 image, 35-45 us); fp32: 4.3e13 (16x16 image); bf16 D 64:
+//   0.90e15 (the video block problem at head_dim 64, 8.7 ms).
 double family_rate(Family fam, int head_dim) {
   switch (fam) {
     case Family::MFMA16: return head_dim == 128 ? 1.15e15 : 0.90e15;
-    case Family::FP8: return 1.55e15;
+    case Family::FP8: return 1.79e15;
     case Family::F32: return 4.3e13;
   }
   return 1e15;
