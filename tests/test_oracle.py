@@ -308,6 +308,41 @@ def test_tile_map_against_nd_brute_force(grid, window, stride, tq, tk):
     assert pr.sum() == total == math.prod(grid) * math.prod(window)
 
 
+@pytest.mark.parametrize("L,w,s,tq,tk", [(11, 4, 2, 4, 2), (17, 6, 3, 8, 4), (9, 9, 1, 4, 8), (5, 1, 1, 2, 2)])
+def test_tile_pairs_1d_against_key_sets(L, w, s, tq, tk):
+    # the per-axis pair counts against the 1-D key sets, tile by tile, and
+    # the invariant that every query holds exactly w keys
+    pairs, vq, vk = oracle.tile_pairs_1d(L, w, s, tq, tk)
+    want = np.zeros_like(pairs)
+    for i in range(L):
+        for j in oracle.key_set((0, 0, i), (1, 1, L), (1, 1, w), (1, 1, s)):
+            want[i // tq, int(j) // tk] += 1
+    np.testing.assert_array_equal(pairs, want)
+    assert pairs.sum() == L * w
+    assert vq.sum() == L and vk.sum() == L
+
+
+def test_effective_flops_counts_attended_pairs():
+    # 4 D FLOPs (QK^T and PV multiply-adds) per attended (query, key) pair,
+    # counted by enumerating the key sets; window = grid gives dense attention
+    grid, window, stride, b, h, d = (3, 5, 6), (2, 3, 4), (1, 3, 2), 2, 3, 16
+    pairs = sum(len(oracle.key_set(np.unravel_index(i, grid), grid, window, stride))
+                for i in range(math.prod(grid)))
+    assert oracle.effective_flops(b, h, grid, window, d) == 4.0 * b * h * d * pairs
+    n = math.prod(grid)
+    assert oracle.effective_flops(1, 1, grid, grid, d) == 4.0 * n * n * d
+
+
+def test_kv_tile_is_full_against_slot_coordinates():
+    # a KV tile is full iff its last slot along every axis is inside the grid
+    grid, tile = (3, 10, 12), (2, 4, 8)
+    n = [-(-L // t) for L, t in zip(grid, tile)]
+    want = [all((c + 1) * t <= L for c, t, L in zip(cc, tile, grid))
+            for cc in itertools.product(*[range(k) for k in n])]
+    np.testing.assert_array_equal(oracle.kv_tile_is_full(grid, tile), np.array(want))
+    assert oracle.kv_tile_is_full((4, 8, 8), (2, 4, 8)).all()
+
+
 def test_video_block_config_is_perfectly_block_sparse():
     # GNA page sections 1.1 and 3.1: at 91 % sparsity the speed-up matches the
     # FLOP reduction, i.e. the KV tiles align with the windows and no
