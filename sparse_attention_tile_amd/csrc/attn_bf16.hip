@@ -15,12 +15,14 @@
 // * Two wavefronts per SIMD, 32 queries per wavefront, NW wavefronts per
 //   workgroup (Q tile = 32 NW queries).  While one wave of a SIMD runs its
 //   softmax on the VALU, the other keeps the matrix core busy; each wave
-//   holds its Q operand in registers for the whole kernel and its O
-//   accumulators in the accumulation registers.
+//   holds its Q operand and its O accumulators in registers for the whole
+//   kernel.
 // * The transposed products are used: S^T = K Q^T and O^T = V^T P^T on
 //   v_mfma_f32_32x32x16_bf16.  In the C layout of S^T a lane holds one query
-//   and 16 keys, so the row max needs one cross-half exchange
-//   (v_permlane32_swap) and the row sum stays in-lane.  K rows are fed to
+//   and 16 keys: the lazy-rescale test compares each lane half's block
+//   maximum with the running one, the cross-half exchange
+//   (v_permlane32_swap) runs only when a rescale happens, and the row sum
+//   stays in-lane.  K rows are fed to
 //   the MFMA in a permuted order so that those 16 accumulators come out as
 //   two runs of 8 consecutive keys, which is exactly the B-operand layout of
 //   the P V product: P goes from registers to the next MFMA with no LDS trip.
