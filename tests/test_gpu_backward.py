@@ -43,6 +43,10 @@ SMALL = [
     ("video_sliding", dict(batch=2, heads=2, grid=(5, 19, 27), window=(3, 7, 9), stride=(1, 2, 3))),
     ("video_sliding", dict(batch=1, heads=2, grid=(5, 19, 27), window=(3, 7, 9), stride=(1, 2, 3), head_dim=64)),
     ("video_block", dict(heads=2, grid=(8, 16, 24), window=(6, 8, 8), stride=(4, 4, 4))),
+    ("img64_sliding", dict(batch=1, heads=2, grid=(1, 1, 1000), window=(1, 1, 65), stride=(1, 1, 1))),  # 1-D
+    ("img64_block", dict(batch=1, heads=2, grid=(1, 1, 1000), window=(1, 1, 64), stride=(1, 1, 32))),
+    ("img64_sliding", dict(batch=1, heads=2, grid=(1, 24, 40), window=(1, 9, 17), stride=(1, 1, 8),
+                           head_dim=128)),                                   # anisotropic window / stride
 ]
 
 
