@@ -18,6 +18,7 @@ CASES = [
     ("img64_sliding", {}, 5),                                                    # 2-D, D 64
     ("video_sliding", dict(batch=2, heads=2, grid=(5, 19, 27)), 7),              # ragged: padded tiles
     ("video_block", dict(heads=2, grid=(3, 16, 24)), 3),
+    ("img64_sliding", dict(batch=1, heads=2, grid=(1, 1, 1500)), 4),             # 1-D, last tiles padded
 ]
 
 
