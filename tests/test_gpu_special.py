@@ -282,6 +282,44 @@ def test_forward_replays_in_a_hip_graph(na, path):
         assert torch.equal(f.out, out_e) and torch.equal(f.lse, lse_e)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_rising_scores_rescale_every_block(na, path, dtype):
+    # Scores that grow block by block along the key sequence (a 1-D grid,
+    # window = grid): each 32-key block's scores sit 16 (in log2 units) above
+    # the previous block's, far more than the lazy-rescale threshold, so the
+    # rescale branch runs on every block; inside a block they are nearly
+    # flat, so the softmax spreads over the last block's keys.  out and lse
+    # must still match the oracle.
+    from synth import quantize_e4m3
+    if dtype == "fp8" and path != "qo":
+        pytest.skip("fp8 runs form 1 only")
+    D = 64 if dtype == "bf16" else 128
+    wl = WORKLOADS["img64_sliding" if dtype == "bf16" else "img256_block_fp8"].with_(
+        name="rising", batch=1, heads=2, grid=(1, 1, 2048), window=(1, 1, 2048), stride=(1, 1, 1), head_dim=D,
+        seed=4242)
+    say(f"[special] rising scores {dtype} ({path})")
+    n = 2048
+    g = torch.Generator("cpu").manual_seed(wl.seed)
+    # q . k_j * scale * log2(e) = 16 * (j // 32) plus a little noise
+    step = 16.0 / math.log2(math.e) / (wl.scale * D)
+    q = torch.ones((1, 1, 1, n, 2, D))
+    lev = (torch.arange(n) // 32).to(torch.float32) * step
+    k = lev.reshape(1, 1, 1, n, 1, 1).expand(1, 1, 1, n, 2, D).clone()
+    k = k + 0.01 * torch.randn(k.shape, generator=g)
+    v = torch.randn((1, 1, 1, n, 2, D), generator=g)
+    if dtype == "bf16":
+        qc, kc, vc = (x.to(torch.bfloat16) for x in (q, k, v))
+        sc = (1.0, 1.0, 1.0)
+    else:
+        (qc, s0), (kc, s1), (vc, s2) = (quantize_e4m3(x) for x in (q, k, v))
+        sc = (s0, s1, s2)
+    out, lse, _ = run_hip(na, wl, qc.cuda(), kc.cuda(), vc.cuda(), sc)
+    eo, el = compare(wl, qc, kc, vc, sc, out, lse)
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    to, tl = TOL[dtype]
+    assert eo <= to and el <= tl
+
+
 @pytest.mark.parametrize("name", ["video_block", "img256_block_fp8"])
 def test_full_size_forward_is_deterministic(na, path, name):
     # The kernels use no atomics and a fixed visiting order, so repeated calls
