@@ -31,6 +31,24 @@ struct TileGeom {
   int cpr_lg;          // log2 of 16-byte chunks per token row
 };
 
+// Work item of this workgroup: one tile of one (batch, head), heads fastest,
+// so the workgroups in flight at once cover every head of a few tiles and
+// together read (or write) whole grid-order token rows (heads x D) instead of
+// one head's slice of many rows.  lin = (batch, head) x tiles + tile is the
+// tile's slot in tile order.
+struct TileBlock {
+  int tile, bh;
+  size_t lin;
+};
+__device__ inline TileBlock tile_block(const TileGeom& g) {
+  const int nbh = gridDim.x / g.ntiles;
+  TileBlock w;
+  w.bh = blockIdx.x % nbh;
+  w.tile = blockIdx.x / nbh;
+  w.lin = (size_t)w.bh * g.ntiles + w.tile;
+  return w;
+}
+
 __device__ inline void tile_origin(const TileGeom& g, int tile, int& t0, int& y0, int& x0) {
   const int a2 = tile % g.n2;
   const int rest = tile / g.n2;
@@ -44,8 +62,9 @@ __device__ inline void tile_origin(const TileGeom& g, int tile, int& t0, int& y0
 // grid -> tile order, one 16-byte chunk per thread step
 __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restrict__ x, uint4* __restrict__ xt,
                                                            TileGeom g) {
-  const int tile = blockIdx.x % g.ntiles;
-  const int bh = blockIdx.x / g.ntiles;
+  const TileBlock wb = tile_block(g);
+  const int tile = wb.tile;
+  const int bh = wb.bh;
   const int b = bh / g.heads;
   const int h = bh % g.heads;
   int t0, y0, x0;
@@ -53,7 +72,7 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restri
   const int ttok_lg = g.lg0 + g.lg1 + g.lg2;
   const int total = 1 << (ttok_lg + g.cpr_lg);
   const int cmask = (1 << g.cpr_lg) - 1;
-  uint4* dst = xt + ((size_t)blockIdx.x << (ttok_lg + g.cpr_lg));
+  uint4* dst = xt + (wb.lin << (ttok_lg + g.cpr_lg));
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
     const int p = e >> g.cpr_lg;
     const int c = e & cmask;
@@ -73,8 +92,9 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint4* __restri
 // tile -> grid order (padding dropped)
 __global__ __launch_bounds__(256) void unpermute_rows_kernel(const uint4* __restrict__ xt, uint4* __restrict__ x,
                                                              TileGeom g) {
-  const int tile = blockIdx.x % g.ntiles;
-  const int bh = blockIdx.x / g.ntiles;
+  const TileBlock wb = tile_block(g);
+  const int tile = wb.tile;
+  const int bh = wb.bh;
   const int b = bh / g.heads;
   const int h = bh % g.heads;
   int t0, y0, x0;
@@ -82,7 +102,7 @@ __global__ __launch_bounds__(256) void unpermute_rows_kernel(const uint4* __rest
   const int ttok_lg = g.lg0 + g.lg1 + g.lg2;
   const int total = 1 << (ttok_lg + g.cpr_lg);
   const int cmask = (1 << g.cpr_lg) - 1;
-  const uint4* src = xt + ((size_t)blockIdx.x << (ttok_lg + g.cpr_lg));
+  const uint4* src = xt + (wb.lin << (ttok_lg + g.cpr_lg));
   for (int e = threadIdx.x; e < total; e += blockDim.x) {
     const int p = e >> g.cpr_lg;
     const int c = e & cmask;
@@ -105,8 +125,9 @@ __global__ __launch_bounds__(256) void permute_transpose_kernel(const uint4* __r
                                                                 TileGeom g, int D) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
-  const int tile = blockIdx.x % g.ntiles;
-  const int bh = blockIdx.x / g.ntiles;
+  const TileBlock wb = tile_block(g);
+  const int tile = wb.tile;
+  const int bh = wb.bh;
   const int b = bh / g.heads;
   const int h = bh % g.heads;
   int t0, y0, x0;
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(256) void permute_transpose_kernel(const uint4* __r
   __syncthreads();
   // store [D][TT]: chunk e covers tokens (e % (TT/E))*E .. +E-1 of row d
   const int cpd = TT / E;  // chunks per output row
-  uint4* dst = xt + (size_t)blockIdx.x * (size_t)(TT * cpr);
+  uint4* dst = xt + wb.lin * (size_t)(TT * cpr);
   for (int e = threadIdx.x; e < D * cpd; e += blockDim.x) {
     const int d = e / cpd;
     const int p0 = (e % cpd) * E;
@@ -155,14 +176,15 @@ __global__ __launch_bounds__(256) void permute_transpose_kernel(const uint4* __r
 // lse: [B, heads, tiles, TT] -> [B, T, H, W, heads]
 __global__ __launch_bounds__(256) void unpermute_lse_kernel(const float* __restrict__ lt, float* __restrict__ l,
                                                             TileGeom g) {
-  const int tile = blockIdx.x % g.ntiles;
-  const int bh = blockIdx.x / g.ntiles;
+  const TileBlock wb = tile_block(g);
+  const int tile = wb.tile;
+  const int bh = wb.bh;
   const int b = bh / g.heads;
   const int h = bh % g.heads;
   int t0, y0, x0;
   tile_origin(g, tile, t0, y0, x0);
   const int ttok_lg = g.lg0 + g.lg1 + g.lg2;
-  const float* src = lt + ((size_t)blockIdx.x << ttok_lg);
+  const float* src = lt + (wb.lin << ttok_lg);
   for (int p = threadIdx.x; p < (1 << ttok_lg); p += blockDim.x) {
     const int px = p & ((1 << g.lg2) - 1);
     const int py = (p >> g.lg2) & ((1 << g.lg1) - 1);
