@@ -14,10 +14,11 @@ from synth import WORKLOADS, make_qkv, sample_queries
 pytestmark = pytest.mark.gpu
 
 # Max-abs error over max |reference| per gradient tensor.  The kernel rounds
-# P and dS to bf16 before the matrix products (relative 2^-9 each), uses the
-# bf16 forward output in D_i = <dout_i, out_i>, and rounds dq, dk, dv to bf16;
-# sums over thousands of such terms keep the error at a few 2^-9 of the
-# largest entries.  1.5e-2 leaves room over the measured ~4e-3.
+# P and dS to bf16 before the matrix products (8 significant bits: relative
+# error up to 2^-8 each), uses the bf16 forward output in D_i = <dout_i,
+# out_i>, and rounds dq, dk, dv to bf16; sums over thousands of such terms
+# keep the error at a few 2^-8 of the largest entries.  1.5e-2 leaves room
+# over the measured ~4e-3.
 REL_TOL = 1.5e-2
 
 

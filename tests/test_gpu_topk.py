@@ -98,3 +98,75 @@ def test_topk_video_full_grid_two_heads(na):
     eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
     say(f"  {len(qs)} queries: max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
     assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+U32 = 2.0 ** -24   # unit roundoff of float32
+
+
+def _means64(x, grid, tile):
+    """Per tile: float64 means of x ([B, N, heads, D]) over its real tokens,
+    and a bound on how far the kernel's float32 mean can be from it (tokens
+    summed one by one in in-tile row-major order: each addition errs by at
+    most u |partial sum|; then one division).  Returns [B, heads, nTiles, D]
+    arrays (mean, bound)."""
+    B, N, H, D = x.shape
+    nt = [-(-L // t) for L, t in zip(grid, tile)]
+    pad = np.zeros((B, nt[0] * tile[0], nt[1] * tile[1], nt[2] * tile[2], H, D))
+    cnt = np.zeros(pad.shape[1:4])
+    pad[:, :grid[0], :grid[1], :grid[2]] = x.reshape(B, *grid, H, D)
+    cnt[:grid[0], :grid[1], :grid[2]] = 1.0
+    # [B, tiles, in-tile tokens (row-major), H, D]
+    t = pad.reshape(B, nt[0], tile[0], nt[1], tile[1], nt[2], tile[2], H, D).transpose(0, 1, 3, 5, 2, 4, 6, 7, 8)
+    t = t.reshape(B, -1, tile[0] * tile[1] * tile[2], H, D)
+    n = cnt.reshape(nt[0], tile[0], nt[1], tile[1], nt[2], tile[2]).sum(axis=(1, 3, 5)).reshape(-1)
+    part = np.abs(np.cumsum(t, axis=2))[:, :, 1:].sum(axis=2)          # sum_i |S_i|
+    mean = t.sum(axis=2) / n[None, :, None, None]
+    bound = U32 * part / n[None, :, None, None] + U32 * np.abs(mean)
+    return mean.transpose(0, 2, 1, 3), bound.transpose(0, 2, 1, 3)
+
+
+def _score_bounds(qm, dq, km, dk):
+    """float64 scores <qm_a, km_c> and a bound on the float32 evaluation's
+    error: input errors, one rounding per product and u |partial sum| per
+    addition over the head dimension (in order); doubled for second-order
+    terms.  qm [nQ, D], km [nK, D]."""
+    s = qm @ km.T
+    err = np.abs(dq) @ np.abs(km).T + np.abs(qm) @ np.abs(dk).T + U32 * (np.abs(qm) @ np.abs(km).T)
+    for a0 in range(0, qm.shape[0], 32):
+        prod = qm[a0:a0 + 32, None, :] * km[None, :, :]
+        err[a0:a0 + 32] += U32 * np.abs(np.cumsum(prod, axis=-1))[..., 1:].sum(axis=-1)
+    return s, 2.0 * err
+
+
+@pytest.mark.parametrize("name,kw,keep", CASES + [("video_block", dict(heads=2, seed=606), 81)])
+def test_topk_selection_is_top_k_of_float64_scores(na, name, kw, keep):
+    # tutorial ("Video-generation inference speed-up: sparse attention
+    # configuration tutorial") section 6: score the blocks by their means and
+    # keep the best.  The kept set must be the top-k of the float64 scores
+    # <mean q, mean k> on every row whose gap at the cut exceeds the float32
+    # evaluation's error bound for the two scores there.
+    wl = WORKLOADS[name].with_(**kw) if "seed" in kw else _wl(name, kw)
+    say(f"[topk] float64 top-k {wl.name} grid={wl.grid} keep={keep}")
+    qc, kc, vc, _ = make_qkv(wl, device="cpu")
+    idx, _ = na.topk_select(qc.cuda(), kc.cuda(), keep)
+    tq, tk = na.na_topk_tiles(wl.grid, wl.head_dim, na.NA_BF16)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    f = lambda x: x.to(torch.float64).numpy().reshape(B, -1, H, D)
+    qm, dq = _means64(f(qc), wl.grid, tq)
+    km, dk = _means64(f(kc), wl.grid, tk)
+    gpu = idx.cpu().numpy().reshape(B, H, -1, keep)
+    checked = rows = 0
+    for b in range(B):
+        for h in range(H):
+            s64, eps = _score_bounds(qm[b, h], dq[b, h], km[b, h], dk[b, h])
+            for a in range(s64.shape[0]):
+                rows += 1
+                order = np.argsort(-s64[a], kind="stable")
+                if keep < len(order):
+                    gap = s64[a, order[keep - 1]] - s64[a, order[keep]]
+                    if gap <= eps[a, order[keep - 1]] + eps[a, order[keep]]:
+                        continue
+                checked += 1
+                assert set(gpu[b, h, a].tolist()) == set(order[:keep].tolist()), (b, h, a)
+    say(f"  {checked} of {rows} rows checked ({100.0 * checked / rows:.1f} %)")
+    assert checked >= 0.5 * rows
