@@ -409,6 +409,33 @@ na_status na_backward(const void* q, const void* k, const void* v,
                       const int stride[3], float scale, na_dtype dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the fixed device buffer na_forward_noalloc keeps its tile map in
+ * (one per GPU, held until the process ends). */
+#define NA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* na_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * calls no hipMalloc / hipFree and allocates no device memory: the tile map
+ * the kernel walks goes into a fixed device buffer of
+ * NA_NOALLOC_SCRATCH_BYTES per GPU, copied there (hipMemcpyAsync on
+ * `stream`, from a host-side map the library builds and caches on the first
+ * call for a geometry) before the kernel on every call.
+ * It computes what na_forward's form 2 computes (bf16, head_dim 64 or 128,
+ * no workspace: the kernel reads q, k, v and writes out, lse in grid order),
+ * bit for bit.  Other dtypes or head dims: NA_ERR_UNSUPPORTED.  A problem
+ * whose tile map (4 bytes per Q tile twice, plus 4 per listed KV tile, each
+ * part rounded up to 256 bytes) exceeds NA_NOALLOC_SCRATCH_BYTES is refused
+ * with NA_ERR_UNSUPPORTED before anything is enqueued.
+ * Every call on one GPU shares that GPU's buffer, which keeps the last
+ * call's contents: calls that overlap on one GPU (different streams, no
+ * ordering between them) race and may produce wrong results.
+ * Arguments, layouts and other errors as for na_forward. */
+na_status na_forward_noalloc(const void* q, const void* k, const void* v,
+                             void* out, float* lse, int batch, int heads,
+                             int head_dim, const int grid[3],
+                             const int window[3], const int stride[3],
+                             float scale, na_dtype dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

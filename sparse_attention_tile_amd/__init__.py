@@ -26,8 +26,12 @@ SYMBOLS = (
     "na_forward_mode", "na_last_error",
     "na_release_cache", "na_forward", "na_permute", "na_unpermute", "na_unpermute_lse", "na_attend_tiled",
     "na_attend_kv_tiled", "na_backward_workspace_bytes", "na_backward", "na_topk_tiles",
-    "na_topk_workspace_bytes", "na_topk_select", "na_topk_forward",
+    "na_topk_workspace_bytes", "na_topk_select", "na_topk_forward", "na_forward_noalloc",
 )
+
+# NA_NOALLOC_SCRATCH_BYTES of na.h: the fixed per-GPU device buffer of
+# na_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class NAError(RuntimeError):
@@ -99,6 +103,7 @@ def load():
                             _i),
         "na_backward": ([_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _p,
                          ctypes.c_size_t, _p], _i),
+        "na_forward_noalloc": ([_p, _p, _p, _p, _p, _i, _i, _i, I3, I3, I3, ctypes.c_float, _i, _p], _i),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -198,6 +203,11 @@ def na_forward(q, k, v, out, lse, batch, heads, head_dim, grid, window, stride, 
     qs = (ctypes.c_float * 3)(*qkv_scale) if qkv_scale is not None else None
     _check(load().na_forward(q, k, v, out, lse, batch, heads, head_dim, _i3(grid), _i3(window), _i3(stride),
                              scale, dtype, qs, workspace, workspace_bytes, stream))
+
+
+def na_forward_noalloc(q, k, v, out, lse, batch, heads, head_dim, grid, window, stride, scale, dtype, stream):
+    _check(load().na_forward_noalloc(q, k, v, out, lse, batch, heads, head_dim, _i3(grid), _i3(window),
+                                     _i3(stride), scale, dtype, stream))
 
 
 def na_permute(x, xt, batch, heads, head_dim, grid, tile, elem_bytes, transpose, stream):

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libna.so")
 
 SOURCES = ["tilemap.cpp", "na_api.cpp", "permute.hip", "attn_f32.hip", "attn_bf16.hip", "attn_fp8.hip",
-           "attn_bwd.hip", "topk.hip"]
+           "attn_bwd.hip", "topk.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code.

@@ -16,6 +16,7 @@
 #include <string>
 #include <tuple>
 
+#include "forward_buffer.hpp"
 #include "kernels.hpp"
 #include "tilemap.hpp"
 
@@ -97,6 +98,14 @@ using PlanKey = std::tuple<int, int, int, int, int, int, int, int, int, int, int
 std::mutex g_mu;
 std::map<PlanKey, std::unique_ptr<Plan>>& plans() {
   static auto* m = new std::map<PlanKey, std::unique_ptr<Plan>>();
+  return *m;
+}
+
+// Host tile maps of the fixed-buffer forward (na_forward_noalloc), per
+// geometry and tile shapes: host memory only, the map is copied into the
+// device buffer on each call.
+std::map<PlanKey, std::unique_ptr<na::TileMap>>& host_maps() {
+  static auto* m = new std::map<PlanKey, std::unique_ptr<na::TileMap>>();
   return *m;
 }
 
@@ -290,6 +299,7 @@ const char* na_last_error(void) { return g_err.c_str(); }
 void na_release_cache(void) {
   std::lock_guard<std::mutex> lk(g_mu);
   plans().clear();
+  host_maps().clear();
 }
 
 na_status na_choose_tiles(const int grid[3], const int window[3], const int stride[3], int head_dim,
@@ -484,13 +494,14 @@ na_status na_unpermute_lse(const float* lse_t, float* lse, int batch, int heads,
                     "lse unpermute launch");
 }
 
-// Kernel arguments of one problem: geometry, tiles and the plan's map.
-static na::AttnArgs attn_args(const na::Geometry& g, const Plan* plan, const int tq[3], const int tkv[3],
-                              int batch, int heads, int head_dim, float scale) {
+// Kernel arguments of one problem: geometry, tiles and a device tile map.
+static na::AttnArgs attn_args(const na::Geometry& g, const int32_t* qptr, const int32_t* kv_idx,
+                              const int32_t* n_full, const int tq[3], const int tkv[3], int batch, int heads,
+                              int head_dim, float scale) {
   na::AttnArgs a{};
-  a.qptr = plan->d_qptr;
-  a.kv_idx = plan->d_kv;
-  a.n_full = plan->d_nfull;
+  a.qptr = qptr;
+  a.kv_idx = kv_idx;
+  a.n_full = n_full;
   a.batch = batch;
   a.heads = heads;
   a.head_dim = head_dim;
@@ -506,6 +517,12 @@ static na::AttnArgs attn_args(const na::Geometry& g, const Plan* plan, const int
   a.scale = scale;
   a.v_scale = 1.0f;
   return a;
+}
+
+// ... with the map of a cached plan.
+static na::AttnArgs attn_args(const na::Geometry& g, const Plan* plan, const int tq[3], const int tkv[3],
+                              int batch, int heads, int head_dim, float scale) {
+  return attn_args(g, plan->d_qptr, plan->d_kv, plan->d_nfull, tq, tkv, batch, heads, head_dim, scale);
 }
 
 static na_status attend_impl(const void* qt, const void* kt, const void* vt, void* ot, float* lse_t, int batch,
@@ -667,6 +684,89 @@ na_status na_forward(const void* q, const void* k, const void* v, void* out, flo
   }
   return NA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// the forward with its tile map in a fixed device buffer (na_forward_noalloc)
+
+}  // extern "C"
+
+namespace na {
+
+// na_forward's form 2 (the kernel reads q, k, v and writes out, lse in grid
+// order) with the tile map copied on `stream` into the device memory
+// get_buffer() returns (buffer_bytes long) instead of a cached allocation.
+// The size check comes before get_buffer is called.
+na_status forward_in_buffer(const void* q, const void* k, const void* v, void* out, float* lse, int batch,
+                            int heads, int head_dim, const int grid[3], const int window[3], const int stride[3],
+                            float scale, na_dtype dtype, void* stream, size_t buffer_bytes,
+                            hipError_t (*get_buffer)(void** ptr)) {
+  g_err.clear();
+  Layout lay;
+  na_status st = check_problem(batch, heads, head_dim, grid, window, stride, (int)dtype, &lay);
+  if (st != NA_OK) return st;
+  if (dtype != NA_BF16 || !na::attn_bf16_grid_io_supported(head_dim))
+    return fail(NA_ERR_UNSUPPORTED, "na_forward_noalloc runs bf16 with head_dim 64 or 128");
+  if (batch == 0 || heads == 0) return NA_OK;
+  if (!q || !k || !v || !out) return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be non-null");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(NA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(NA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  st = check_scales(scale, dtype, nullptr);
+  if (st != NA_OK) return st;
+  const na::Geometry g = make_geom(grid, window, stride);
+  const na::TileCounts c = na::count_tiles(g, lay.tq, lay.tkv);
+  const size_t off_kv = round256((size_t)(c.n_q_tiles + 1) * sizeof(int32_t));
+  const size_t off_nf = off_kv + round256((size_t)std::max<int64_t>(c.nnz, 1) * sizeof(int32_t));
+  const size_t need = off_nf + round256((size_t)c.n_q_tiles * sizeof(int32_t));
+  if (need > buffer_bytes)
+    return fail(NA_ERR_UNSUPPORTED, "the tile map of this problem needs " + std::to_string(need) +
+                                        " bytes, more than the fixed " + std::to_string(buffer_bytes) +
+                                        "-byte device buffer of na_forward_noalloc");
+  const na::TileMap* map = nullptr;
+  {
+    const char* fm = std::getenv("NA_FORCE_MASK");
+    const int force_mask = (fm && fm[0] == '1') ? 1 : 0;
+    PlanKey key{-1,        g.L[0],    g.L[1],    g.L[2],    g.w[0], g.w[1], g.w[2],
+                g.s[0],    g.s[1],    g.s[2],    lay.tq[0], lay.tq[1], lay.tq[2],
+                lay.tkv[0], lay.tkv[1], lay.tkv[2], force_mask, 0,        0};
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto& hm = host_maps();
+    auto it = hm.find(key);
+    if (it == hm.end()) {
+      auto m = std::make_unique<na::TileMap>(na::build_tile_map(g, lay.tq, lay.tkv));
+      if (force_mask) std::fill(m->n_full.begin(), m->n_full.end(), 0);
+      it = hm.emplace(key, std::move(m)).first;
+    }
+    map = it->second.get();
+  }
+  void* base = nullptr;
+  if ((st = hip_status(get_buffer(&base), "device address of the fixed buffer"))) return st;
+  char* b = static_cast<char*>(base);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t nq = map->n_full.size(), nnz = map->kv_idx.size();
+  if ((st = hip_status(hipMemcpyAsync(b, map->qptr.data(), (nq + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s),
+                       "tile map copy")) ||
+      (nnz && (st = hip_status(hipMemcpyAsync(b + off_kv, map->kv_idx.data(), nnz * sizeof(int32_t),
+                                               hipMemcpyHostToDevice, s),
+                               "tile map copy"))) ||
+      (st = hip_status(hipMemcpyAsync(b + off_nf, map->n_full.data(), nq * sizeof(int32_t), hipMemcpyHostToDevice, s),
+                       "tile map copy")))
+    return st;
+  na::AttnArgs a = attn_args(g, reinterpret_cast<const int32_t*>(b), reinterpret_cast<const int32_t*>(b + off_kv),
+                             reinterpret_cast<const int32_t*>(b + off_nf), lay.tq, lay.tkv, batch, heads, head_dim,
+                             scale);
+  a.qt = q;
+  a.kt = k;
+  a.vt = v;
+  a.ot = out;
+  a.lse_t = lse;
+  a.io_mode = na::IO_GRID;
+  return hip_status(na::launch_attn_bf16(a, s), "attention launch");
+}
+
+}  // namespace na
+
+extern "C" {
 
 // ---------------------------------------------------------------------------
 // backward

@@ -257,3 +257,30 @@ def test_launch_size_limits_rejected(na):
         na.NA_ERR_UNSUPPORTED
     assert lib.na_unpermute(fake, fake, 1, 1, 128, big, I3(1, 8, 8), 2, None) == na.NA_ERR_UNSUPPORTED
     assert lib.na_workspace_bytes(1, 64, 128, big, one, one, na.NA_BF16) == 0
+
+
+def test_noalloc_arguments_rejected(na):
+    # na_forward_noalloc validates everything, the tile map's size against
+    # its fixed device buffer included, before any HIP call
+    lib = na.load()
+    I3 = na.I3
+    fake = 1 << 20
+
+    def fwd(dt=na.NA_BF16, D=128, grid=I3(1, 16, 16), window=I3(1, 5, 5), q=fake, out=fake, B=1):
+        return lib.na_forward_noalloc(q, fake, fake, out, None, B, 2, D, grid, window, I3(1, 1, 1), 0.125, dt, None)
+
+    assert fwd(dt=na.NA_FP8_E4M3) == na.NA_ERR_UNSUPPORTED
+    assert fwd(dt=na.NA_F32, D=32) == na.NA_ERR_UNSUPPORTED
+    assert fwd(D=48) == na.NA_ERR_UNSUPPORTED
+    assert fwd(window=I3(1, 17, 5)) == na.NA_ERR_INVALID_ARG
+    assert fwd(q=None) == na.NA_ERR_INVALID_ARG
+    assert fwd(out=fake + 8) == na.NA_ERR_INVALID_ARG
+    assert fwd(B=0, q=None) == na.NA_OK
+    # dense attention over 600,000 tokens: its tile map (millions of entries)
+    # does not fit the fixed buffer
+    n = 600000
+    tq, tk = na.na_choose_tiles((1, 1, n), (1, 1, n), (1, 1, 1), 128, na.NA_BF16)
+    nnz = math.prod(-(-n // t) for t in (tq[2],)) * (-(-n // tk[2]))
+    assert 4 * nnz > na.NOALLOC_SCRATCH_BYTES
+    assert fwd(grid=I3(1, 1, n), window=I3(1, 1, n)) == na.NA_ERR_UNSUPPORTED
+    assert "fixed" in na.na_last_error()
