@@ -39,7 +39,8 @@ def hipcc() -> str:
 # The attention kernels handle no NaN inputs specially and need no IEEE
 # signalling-NaN quieting in min/max: without it fmaxf maps to v_max3_f32
 # with no canonicalising moves.
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"], "attn_bwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+ "attn_bwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "attn_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 

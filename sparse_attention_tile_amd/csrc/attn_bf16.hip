@@ -51,10 +51,12 @@ namespace {
 
 // Lazy rescaling: move the reference max m only when the block max exceeds
 // it by more than thr (= 8 / c2, a factor 2^8 after exp2); then scale l and
-// O by exp2((m_old - m_new) c2).  The branch is wave-uniform and rare.
+// O by exp2((m_old - m_new) c2) and update the exponent offset nref = -m c2
+// (kept with m rather than recomputed per block).  The branch is
+// wave-uniform and rare.
 template <int DB>
-__device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, float& l, f32x16 (&o)[DB], float c2,
-                                                  float thr) {
+__device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, float& nref, float& l, f32x16 (&o)[DB],
+                                                  float c2, float thr) {
   // one serial chain of three-input maxima (v_max3_f32: 8 instructions)
   float bm = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
@@ -72,6 +74,7 @@ __device__ __forceinline__ void rescale_if_needed(const f32x16& s, float& m, flo
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] *= alpha;
     m = mn;
+    nref = mn == -INFINITY ? 0.f : -mn * c2;
   }
 }
 
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
 #pragma unroll
   for (int d = 0; d < DB; ++d) o[d] = f32x16{};
   float m = -INFINITY, l = 0.f;
+  float nref = 0.f;   // -m c2 (0 while every key so far is masked: then p = 0)
 
   // The tile map is read-only for the whole launch: read it through the
   // constant address space so the loads are scalar (s_load, lgkmcnt) and never
@@ -298,12 +302,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   // stage the next tile's copy writes (nb) never overlap; the compiler then
   // knows the in-flight copy cannot feed this tile's LDS reads and issues no
   // wait on it before them (it cannot see this for the transposing reads).
+  // mask(s, kb) applies the window mask to block kb's scores (a no-op on
+  // full tiles).
   auto tile_body = [&](const unsigned char* __restrict__ Ks, const unsigned char* __restrict__ Vs,
-                       lds_u8* __restrict__ nb, uint64_t vmask, auto bnd) {
-    constexpr bool BOUNDARY = decltype(bnd)::value;
+                       lds_u8* __restrict__ nb, auto&& mask) {
     f32x16 s = qk_block<D, KROW>(Ks, 0, krow0, kswz, hh, qr);
-    if constexpr (BOUNDARY) apply_mask(s, vmask, 0);
-    rescale_if_needed(s, m, l, o, c2, thr);
+    mask(s, 0);
+    rescale_if_needed(s, m, nref, l, o, c2, thr);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       // LLVM's single-wave MFMA / LDS-read interleaving strategy for this
@@ -313,7 +318,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
       f32x16 sn;
       if (kb + 1 < KB) sn = qk_block<D, KROW>(Ks, kb + 1, krow0, kswz, hh, qr);
       // ---- P = exp2(S c2 - m c2) in bf16; accumulator i <-> key 16*(i/8) + 8*hh + i%8
-      const float nref = m == -INFINITY ? 0.f : -m * c2;   // every key so far masked: p = 0
       bf16x8 pv[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) pv[i >> 3][i & 7] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[i], c2, nref));
@@ -341,8 +345,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
         }
       }
       if (kb + 1 < KB) {
-        if constexpr (BOUNDARY) apply_mask(sn, vmask, kb + 1);
-        rescale_if_needed(sn, m, l, o, c2, thr);
+        mask(sn, kb + 1);
+        rescale_if_needed(sn, m, nref, l, o, c2, thr);
         s = sn;
       }
     }
@@ -391,6 +395,33 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
                              p.lk2, km1, km2, ksh);
   };
 
+  // Boundary tiles 8 or 16 keys wide along W (not paired): each 8-key group
+  // a lane holds lies in one key row (t, y) of the tile, at an x offset that
+  // is the same for both of the lane's groups and every block (0 for 8-wide
+  // tiles, 8 hh for 16-wide ones).  So a key is inside the lane's window iff
+  // its row is and its x is: the 8 x tests are made once per tile (lane
+  // masks, kept in scalar registers), the row test once per group and block,
+  // then one select per score.  Same masked set as boundary_mask / apply_mask.
+  auto row_masker = [&](int kv) {
+    const int k2 = (kv % p.nk2) << p.lk2;
+    const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
+    const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
+    const int x0 = k2 + (p.lk2 == 4 ? 8 * hh : 0) - st2;
+    bool xv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xv[j] = (unsigned)(x0 + j) < (unsigned)p.w2;
+    return [=, &p](f32x16& sc, int kb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int row = (32 * kb + 16 * c + 8 * hh) >> p.lk2;   // key row of accumulators 8 c .. 8 c + 7
+        const bool rv = ((unsigned)(k0 + (row >> p.lk1) - st0) < (unsigned)p.w0) &
+                        ((unsigned)(k1 + (row & km1) - st1) < (unsigned)p.w1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sc[8 * c + j] = (rv && xv[j]) ? sc[8 * c + j] : -INFINITY;
+      }
+    };
+  };
+
   // Three homogeneous loops (padding-only waves copy; full tiles; boundary
   // tiles), so the accumulators flow through simple loop phis.
   const unsigned char* Ks;
@@ -406,19 +437,26 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_bf16_kernel(KParams p) {
   } else {
     for (int j = beg; j < jfull; j += TSTEP) {
       begin_tile(j, Ks, Vs);
-      tile_body(Ks, Vs, nbuf, 0ull, std::integral_constant<bool, false>{});
+      tile_body(Ks, Vs, nbuf, [](f32x16&, int) {});
     }
-    for (int j = jfull; j < end; j += TSTEP) {
-      const int kv = begin_tile(j, Ks, Vs);
-      uint64_t vmask;
-      if constexpr (PAIRED) {   // the two tiles' masks side by side (groups 0..3, 4..7)
-        const uint64_t ma = kv_tile_mask(kv_idx[j], std::integral_constant<int, 4>{});
-        const uint64_t mb = j + 1 < end ? kv_tile_mask(kv_idx[j + 1], std::integral_constant<int, 4>{}) : 0ull;
-        vmask = ma | (mb << 32);
-      } else {
-        vmask = kv_tile_mask(kv, std::integral_constant<int, KVT / 16>{});
+    if (!PAIRED && !GKV && KVT == 128 && (p.lk2 == 3 || p.lk2 == 4)) {
+      for (int j = jfull; j < end; j += TSTEP) {
+        const int kv = begin_tile(j, Ks, Vs);
+        tile_body(Ks, Vs, nbuf, row_masker(kv));
       }
-      tile_body(Ks, Vs, nbuf, vmask, std::integral_constant<bool, true>{});
+    } else {
+      for (int j = jfull; j < end; j += TSTEP) {
+        const int kv = begin_tile(j, Ks, Vs);
+        uint64_t vmask;
+        if constexpr (PAIRED) {   // the two tiles' masks side by side (groups 0..3, 4..7)
+          const uint64_t ma = kv_tile_mask(kv_idx[j], std::integral_constant<int, 4>{});
+          const uint64_t mb = j + 1 < end ? kv_tile_mask(kv_idx[j + 1], std::integral_constant<int, 4>{}) : 0ull;
+          vmask = ma | (mb << 32);
+        } else {
+          vmask = kv_tile_mask(kv, std::integral_constant<int, KVT / 16>{});
+        }
+        tile_body(Ks, Vs, nbuf, [vmask](f32x16& sc, int kb) { apply_mask(sc, vmask, kb); });
+      }
     }
   }
   // the last step's copy must land before the workgroup's LDS is released

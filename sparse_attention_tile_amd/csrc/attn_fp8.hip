@@ -130,6 +130,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   f32x4_t osum = {};                      // every element: sum of the stored P of this lane's query
   float m = -INFINITY;
+  // exponent offset of P: -m c2 + log2 of the P scale (the m term is 0 while
+  // every key so far is masked); kept with m, updated when m moves
+  float nref = kPScaleLog2;
   // A operand of the row-sum product (16x16x128): e4m3 1.0 where the lane
   // group holds the keys of the query this output row belongs to, else 0
   const int selv = (((lane >> 2) ^ (lane >> 4)) & 1) ? 0 : 0x38383838;
@@ -231,6 +234,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
       for (int d = 0; d < DB; ++d) o[d] *= alpha;
       osum *= alpha;
       m = mn;
+      nref = (mn == -INFINITY ? 0.f : -mn * c2) + kPScaleLog2;
     }
   };
 
@@ -238,7 +242,6 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   // keys, with the row sums through the selector product
   auto softmax_pv = [&](const f32x16& s0, const f32x16& s1, const unsigned char* Vs, int st) {
     // P bytes: byte j < 16 is key 16 hh + j of block 2 st, byte 16 + j key 16 hh + j of block 2 st + 1
-    const float nref = (m == -INFINITY ? 0.f : -m * c2) + kPScaleLog2;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_exp2f(fmaf(s0[4 * q], c2, nref)),
