@@ -212,28 +212,34 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void bwd_dq_kernel(BwdParams bp) {
     }
   };
 
-  for (int j = beg; j < end; ++j) {
+  // One loop over the full tiles, then one over the boundary tiles, so each
+  // keeps its own registers (a branch between the two inside one loop made
+  // the compiler spill the values live across it on every tile).
+  auto run_tile = [&](int j, auto bnd) {
+    constexpr bool BOUNDARY = decltype(bnd)::value;
     const int stage = (j - beg) & 1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     const bool copy = j + 1 < end;
     const int kvn = copy ? kv_idx[j + 1] : 0;
-    const int kv = kv_idx[j];
     const unsigned char* Ks = smem + stage * STAGE;
     lds_u8* nb = lds + (stage ^ 1) * STAGE;
     const unsigned char* nk = kbase + (size_t)kvn * TILEB;
     const unsigned char* nv = vbase + (size_t)kvn * TILEB;
-    if (j < beg + nfull) {
-      tile_body(Ks, Ks + TILEB, nb, nk, nv, copy, 0ull, std::integral_constant<bool, false>{});
-    } else {
+    uint64_t vmask = 0;
+    if constexpr (BOUNDARY) {
+      const int kv = kv_idx[j];
       const int k2 = (kv % p.nk2) << p.lk2;
       const int k1 = ((kv / p.nk2) % p.nk1) << p.lk1;
       const int k0 = (kv / (p.nk2 * p.nk1)) << p.lk0;
-      const uint64_t vmask = boundary_mask<KVT / 16>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1,
-                                                     st2, p.w0, p.w1, p.w2, p.lk2, km1, km2, ksh);
-      tile_body(Ks, Ks + TILEB, nb, nk, nv, copy, vmask, std::integral_constant<bool, true>{});
+      vmask = boundary_mask<KVT / 16>([&](int gg) { return 8 * (2 * gg + hh); }, k0, k1, k2, st0, st1, st2, p.w0,
+                                      p.w1, p.w2, p.lk2, km1, km2, ksh);
     }
-  }
+    tile_body(Ks, Ks + TILEB, nb, nk, nv, copy, vmask, bnd);
+  };
+  const int jfull = beg + nfull;
+  for (int j = beg; j < jfull; ++j) run_tile(j, std::integral_constant<bool, false>{});
+  for (int j = jfull; j < end; ++j) run_tile(j, std::integral_constant<bool, true>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   if (!q_valid) return;
