@@ -56,18 +56,20 @@ def time_steps(torch, fn, steps, warmup):
     return per, ev[0].elapsed_time(ev[steps])
 
 
-def kernel_source_hash():
+def kernel_source_hash(family="attn_bf16"):
+    """sha256[:16] over the sources of one attention kernel family
+    ("attn_bf16" or "attn_fp8") and the headers they share."""
     h = hashlib.sha256()
-    for f in ("attn_bf16.hip", "attn_common.hpp", "attn_device.hpp"):
+    for f in (f"{family}.hip", "attn_common.hpp", "attn_device.hpp"):
         with open(os.path.join(ROOT, "sparse_attention_tile_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, src_hash, kform):
+def measured_traffic(workload, src_hash, kform, family="attn_bf16"):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source and form; else None."""
-    path = os.path.join(ROOT, "profiles", f"attn_bf16_{kform.lower()}_{workload}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{family}_{kform.lower()}_{workload}_traffic.json")
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -78,11 +80,11 @@ def measured_traffic(workload, src_hash, kform):
     return d.get("hbm_bytes_per_launch")
 
 
-def measured_mfma(workload, src_hash, kform):
+def measured_mfma(workload, src_hash, kform, family="attn_bf16"):
     """MFMA-busy fraction and clock of the attention kernel from the committed
     rocprofv3 counter summary, if taken on the current kernel source; else
     None."""
-    path = os.path.join(ROOT, "profiles", f"attn_bf16_{kform.lower()}_{workload}_mfma.json")
+    path = os.path.join(ROOT, "profiles", f"{family}_{kform.lower()}_{workload}_mfma.json")
     try:
         with open(path) as fh:
             d = json.load(fh)
@@ -333,11 +335,12 @@ def main():
     computed = 4.0 * B * H * tstats["computed_slots"] * D
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = eff / (kernel_ms * 1e-3) / 1e12
-    src_hash = kernel_source_hash()
     kname = {na.NA_BF16: "attn_bf16_kernel", na.NA_FP8_E4M3: "attn_fp8_kernel", na.NA_F32: "attn_f32_kernel"}[dcode]
+    family = {na.NA_BF16: "attn_bf16", na.NA_FP8_E4M3: "attn_fp8", na.NA_F32: "attn_f32"}[dcode]
+    src_hash = kernel_source_hash(family)
     kform = {0: "IO_TILE", 1: "IO_QO", 2: "IO_GRID"}[mode]
-    traffic = measured_traffic(wl.name, src_hash, kform)
-    mfma = measured_mfma(wl.name, src_hash, kform) if dcode == na.NA_BF16 else None
+    traffic = measured_traffic(wl.name, src_hash, kform, family)
+    mfma = measured_mfma(wl.name, src_hash, kform, family)
     torch_perm_ms = torch_permute_ms(torch, (q, k, v), wl.grid, (tq, tk, tk), st_steps)
 
     result = {
