@@ -267,8 +267,12 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
 
   // One LDS tile: a software pipeline over its 64-key steps -- S^T of step
   // st + 1 is issued before the exponentials of step st, so the wave has
-  // matrix work beside them.
-  auto tile_body = [&](const unsigned char* Ks, const unsigned char* Vs, uint64_t vmask, auto bnd) {
+  // matrix work beside them.  The restrict qualifiers state that the stage
+  // being read (Ks, Vs) and the stage the next tile's copy writes (nb) never
+  // overlap, so the compiler issues no wait on that in-flight copy before
+  // this tile's LDS reads.
+  auto tile_body = [&](const unsigned char* __restrict__ Ks, const unsigned char* __restrict__ Vs,
+                       lds_u8* __restrict__ nb, uint64_t vmask, auto bnd) {
     constexpr bool BOUNDARY = decltype(bnd)::value;
     f32x16 s0 = qk(Ks, 0), s1 = qk(Ks, 1);
     if constexpr (BOUNDARY) {
@@ -278,8 +282,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
     rescale(s0, s1);
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
-      copy_step(nka, nva, nkb, nvb, nbuf, 2 * st);
-      copy_step(nka, nva, nkb, nvb, nbuf, 2 * st + 1);
+      copy_step(nka, nva, nkb, nvb, nb, 2 * st);
+      copy_step(nka, nva, nkb, nvb, nb, 2 * st + 1);
       f32x16 t0, t1;
       if (st + 1 < NSTEP) {
         t0 = qk(Ks, 2 * st + 2);
@@ -349,11 +353,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void attn_fp8_kernel(KParams p) {
   } else {
     for (int j = beg; j < jfull; j += TSTEP) {
       begin_tile(j, Ks, Vs);
-      tile_body(Ks, Vs, 0ull, std::integral_constant<bool, false>{});
+      tile_body(Ks, Vs, nbuf, 0ull, std::integral_constant<bool, false>{});
     }
     for (int j = jfull; j < end; j += TSTEP) {
       begin_tile(j, Ks, Vs);
-      tile_body(Ks, Vs, lds_tile_mask(j), std::integral_constant<bool, true>{});
+      tile_body(Ks, Vs, nbuf, lds_tile_mask(j), std::integral_constant<bool, true>{});
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
