@@ -274,15 +274,15 @@ bool choose_tiles(const Geometry& g, int head_dim, Family fam, int tq[3], int tk
 // rounds of 256 x slots; the time is rounds x one workgroup's average time,
 // plus a launch overhead.  Calibration (one MI355X, kernel ms measured with
 // HIP events; boxes differ by a few per cent):
-//   bf16 D 128: 1.15e15 FLOP/s of computed work on full tiles (91 %-sparse
-//   video, 13.0-13.5 ms); boundary tiles 1.2x (video sliding window, 23.5 %
-//   boundary, 74-75 ms); fp8 D 128: 1.79e15 (4K image, 1.94-1.99 ms); launch
-//   15 us (64x64 image, 35-45 us); fp32: 4.3e13 (16x16 image); bf16 D 64:
-//   0.90e15 (the video block problem at head_dim 64, 8.7 ms).
+//   bf16 D 128: 1.215e15 FLOP/s of computed work on full tiles (91 %-sparse
+//   video, 12.5-13.1 ms); boundary tiles 1.11x (video sliding window, 23.5 %
+//   boundary, 69.7-70.6 ms); fp8 D 128: 1.85e15 (4K image, 1.89-1.92 ms);
+//   launch 15 us (64x64 image, 35-45 us); fp32: 4.3e13 (16x16 image); bf16
+//   D 64: 0.93e15 (the video block problem at head_dim 64, 8.5 ms).
 double family_rate(Family fam, int head_dim) {
   switch (fam) {
-    case Family::MFMA16: return head_dim == 128 ? 1.15e15 : 0.90e15;
-    case Family::FP8: return 1.79e15;
+    case Family::MFMA16: return head_dim == 128 ? 1.215e15 : 0.93e15;
+    case Family::FP8: return 1.85e15;
     case Family::F32: return 4.3e13;
   }
   return 1e15;
@@ -290,7 +290,7 @@ double family_rate(Family fam, int head_dim) {
 
 double predict_kernel_ms(const Geometry& g, int batch, int heads, int head_dim, Family fam, const int tq[3],
                          const int tkv[3], const TileCounts& c) {
-  constexpr double kLaunchMs = 0.015, kBoundary = 0.2;
+  constexpr double kLaunchMs = 0.015, kBoundary = 0.11;
   constexpr int kCUs = 256;
   (void)g;
   const int qtok = tq[0] * tq[1] * tq[2], ktok = tkv[0] * tkv[1] * tkv[2];
