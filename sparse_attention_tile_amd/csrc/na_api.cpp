@@ -789,10 +789,11 @@ na_status check_bwd(int batch, int heads, int head_dim, const int grid[3], const
   if (dtype != NA_BF16 || (head_dim != 64 && head_dim != 128))
     return fail(NA_ERR_UNSUPPORTED, "the backward is built for bf16 with head_dim 64 or 128");
   // 128-query and 128-key tiles, both at least 8 wide along W: the cheapest
-  // such pair of the forward's candidates
+  // such pair of the forward's candidates (with Q tiles padded to 8 along W
+  // when the grid is narrower)
   const na::Geometry g = make_geom(grid, window, stride);
   bool found = false;
-  for (const auto& c : na::tile_candidates(g, head_dim, na::Family::MFMA16)) {
+  for (const auto& c : na::tile_candidates(g, head_dim, na::Family::MFMA16, 8)) {
     if (c.tq[0] * c.tq[1] * c.tq[2] != 128 || c.tkv[0] * c.tkv[1] * c.tkv[2] != 128 || c.tq[2] < 8 ||
         c.tkv[2] < 8)
       continue;

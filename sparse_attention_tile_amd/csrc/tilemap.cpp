@@ -230,14 +230,14 @@ double shape_penalty(Family fam, int qtok, int ktok) {
 
 }  // namespace
 
-std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam) {
+std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam, int min_q_w) {
   std::vector<Opt> qopts, kopts;
   int min_kv_w = 1;
   std::vector<Candidate> out;
   if (!family_options(fam, head_dim, qopts, kopts, min_kv_w)) return out;
   for (const auto& qo : qopts) {
     std::vector<std::array<int, 3>> qs;
-    shapes_with_product(g, qo.tok, qs, 1);
+    shapes_with_product(g, qo.tok, qs, min_q_w);
     for (const auto& ko : kopts) {
       std::vector<std::array<int, 3>> ks;
       shapes_with_product(g, ko.tok, ks, min_kv_w);

@@ -96,7 +96,9 @@ struct Candidate {
 
 // Every candidate the chooser considers, sorted by cost (the first one is
 // what choose_tiles returns).  Empty if the family has no kernel for head_dim.
-std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam);
+// min_q_w: the smallest Q tile extent along W (the backward's dk/dv kernel
+// needs 8; a narrower grid is then padded along W).
+std::vector<Candidate> tile_candidates(const Geometry& g, int head_dim, Family fam, int min_q_w = 1);
 
 // Predicted attention-kernel time (ms) on one MI355X: a per-CU serial model
 // calibrated on the measured kernels (see the constants in tilemap.cpp).

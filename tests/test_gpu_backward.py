@@ -182,3 +182,36 @@ def test_backward_replays_in_a_hip_graph(na):
         torch.cuda.synchronize()
         for t, e in zip(grads, (dq_e, dk_e, dv_e)):
             assert torch.equal(t, e)
+
+
+def _random_bwd_cases():
+    from test_gpu_random import _geometry
+    out = []
+    for i in range(16):
+        rng = np.random.default_rng(8000 + i)
+        grid, window, stride = _geometry(rng)
+        D = int(rng.choice([64, 128]))
+        batch, heads = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        out.append((f"b{i}", grid, window, stride, D, batch, heads))
+    return out
+
+
+RANDOM_BWD = _random_bwd_cases()
+
+
+@pytest.mark.parametrize("name,grid,window,stride,D,batch,heads", RANDOM_BWD, ids=[c[0] for c in RANDOM_BWD])
+def test_backward_random_geometries(na, dkdv, name, grid, window, stride, D, batch, heads):
+    # seeded random 1-/2-/3-D geometries (ragged extents, 1 <= s <= w <= L),
+    # every row of every gradient against the oracle
+    wl = WORKLOADS["img64_sliding"].with_(name=name, batch=batch, heads=heads, grid=grid, window=window,
+                                          stride=stride, head_dim=D, seed=8100 + int(name[1:]))
+    say(f"[bwd] random {name} ({dkdv}) grid={grid} w={window} s={stride} D={D} B={batch} H={heads}")
+    qc, kc, vc, _ = make_qkv(wl, device="cpu")
+    do = _dout(wl, wl.seed + 5)
+    _, _, dq, dk, dv = _run(na, wl, qc.cuda(), kc.cuda(), vc.cuda(), do.cuda())
+    f64 = lambda x: x.to(torch.float64).numpy()
+    rq, rk, rv = oracle.attend_backward(f64(qc), f64(kc), f64(vc), f64(do), grid, window, stride, wl.scale)
+    shape = (batch, math.prod(grid), heads, D)
+    eq, ek, ev = (_rel_err(g.reshape(shape), r) for g, r in ((dq, rq), (dk, rk), (dv, rv)))
+    say(f"  rel err dq={eq:.2e} dk={ek:.2e} dv={ev:.2e}")
+    assert eq <= REL_TOL and ek <= REL_TOL and ev <= REL_TOL
