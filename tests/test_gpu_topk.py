@@ -170,3 +170,45 @@ def test_topk_selection_is_top_k_of_float64_scores(na, name, kw, keep):
                 assert set(gpu[b, h, a].tolist()) == set(order[:keep].tolist()), (b, h, a)
     say(f"  {checked} of {rows} rows checked ({100.0 * checked / rows:.1f} %)")
     assert checked >= 0.5 * rows
+
+
+def _random_topk_cases():
+    from test_gpu_random import _geometry
+    out = []
+    for i in range(16):
+        rng = np.random.default_rng(9000 + i)
+        grid, _, _ = _geometry(rng)
+        D = int(rng.choice([64, 128]))
+        batch, heads = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        out.append((f"t{i}", grid, D, batch, heads, float(rng.uniform(0.0, 1.0))))
+    return out
+
+
+RANDOM_TOPK = _random_topk_cases()
+
+
+@pytest.mark.parametrize("name,grid,D,batch,heads,frac", RANDOM_TOPK, ids=[c[0] for c in RANDOM_TOPK])
+def test_topk_random_geometries(na, name, grid, D, batch, heads, frac):
+    # seeded random 1-/2-/3-D grids (ragged, tiles padded), keep anywhere
+    # from one KV tile to all of them: the kept sets bit for bit, the
+    # attention over them on every query against the oracle
+    wl = WORKLOADS["img64_sliding"].with_(name=name, batch=batch, heads=heads, grid=grid, window=grid,
+                                          stride=(1, 1, 1), head_dim=D, seed=9100 + int(name[1:]))
+    tq, tk = na.na_topk_tiles(grid, D, na.NA_BF16)
+    nk = math.prod(-(-L // t) for L, t in zip(grid, tk))
+    keep = max(1, min(nk, int(round(frac * nk))))
+    say(f"[topk] random {name} grid={grid} D={D} B={batch} H={heads} tiles {tq} / {tk} keep {keep} of {nk}")
+    qc, kc, vc, _ = make_qkv(wl, device="cpu")
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+    idx, nf = na.topk_select(q, k, keep)
+    ridx, rnf, _, _ = _oracle_select(na, wl, qc, kc, keep)
+    assert np.array_equal(idx.cpu().numpy(), ridx) and np.array_equal(nf.cpu().numpy(), rnf)
+    out, lse = na.topk_forward(q, k, v, keep, scale=wl.scale)
+    torch.cuda.synchronize()
+    f = lambda x: x.to(torch.float32).numpy().reshape(batch, -1, heads, D)
+    ro, rl = oracle.topk_attend(f(qc), f(kc), f(vc), grid, tq, tk, keep, wl.scale)
+    go = out.cpu().to(torch.float64).numpy().reshape(ro.shape)
+    gl = lse.cpu().to(torch.float64).numpy().reshape(rl.shape)
+    eo, el = float(np.abs(go - ro).max()), float(np.abs(gl - rl).max())
+    say(f"  max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
+    assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
