@@ -53,3 +53,26 @@ def test_noalloc_matches_forward_on_calls_in_a_row(na):
         eo, el = float(np.abs(go - ro[:, :, 0]).max()), float(np.abs(gl - rl[:, :, 0]).max())
         say(f"  bit-identical to na_forward; max|out-oracle|={eo:.3e} max|lse-oracle|={el:.3e}")
         assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+def test_noalloc_random_geometries_in_a_row(na):
+    # seeded random 1-/2-/3-D geometries, one call after another on the one
+    # buffer (large and small maps alternating): each bit for bit equal to
+    # na_forward's form 2
+    from test_gpu_random import _geometry
+    for i in range(12):
+        rng = np.random.default_rng(9500 + i)
+        grid, window, stride = _geometry(rng)
+        D = int(rng.choice([64, 128]))
+        wl = WORKLOADS["img64_sliding"].with_(name=f"na{i}", batch=int(rng.integers(1, 3)),
+                                              heads=int(rng.integers(1, 4)), grid=grid, window=window,
+                                              stride=stride, head_dim=D, seed=9600 + i)
+        say(f"[noalloc] random {wl.name} grid={grid} w={window} s={stride} D={D} B={wl.batch} H={wl.heads}")
+        qc, kc, vc, _ = make_qkv(wl, device="cpu")
+        q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+        ref_out, ref_lse = na.forward(q, k, v, window, stride, scale=wl.scale, workspace=False)
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:-1], float("nan"), dtype=torch.float32, device=q.device)
+        _noalloc(na, wl, q, k, v, out, lse)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
