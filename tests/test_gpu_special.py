@@ -394,3 +394,54 @@ def test_fp8_error_against_window_size(na, w):
         to = max(to, 2 * u / (1 - u) * float(vc.float().abs().max()) * sc[2])
     say(f"[special] fp8 window {w}: max|out-oracle|={eo:.3e} (bound {to:.3e}) max|lse-oracle|={el:.3e}")
     assert eo <= to and el <= tl
+
+
+def _random_permute_cases():
+    cases = []
+    for i in range(30):
+        rng = np.random.default_rng(3000 + i)
+        nd = int(rng.integers(1, 4))
+        grid = [1, 1, int(rng.integers(1, 40))]
+        if nd >= 2:
+            grid[1] = int(rng.integers(1, 24))
+        if nd == 3:
+            grid[0] = int(rng.integers(1, 9))
+        dtype = [torch.bfloat16, torch.float32, torch.float8_e4m3fn][i % 3]
+        D = int(rng.choice([32, 64, 128]))
+        tt_lg = int(rng.integers(0, 9))            # 1 .. 256 tokens per tile
+        a = int(rng.integers(0, tt_lg + 1))
+        b = int(rng.integers(0, tt_lg - a + 1))
+        tile = (1 << a, 1 << b, 1 << (tt_lg - a - b))
+        eb = torch.tensor([], dtype=dtype).element_size()
+        transpose = bool(rng.random() < 0.6) and (1 << tt_lg) * eb % 16 == 0 and dtype != torch.float32
+        cases.append((f"p{i}", tuple(grid), tile, dtype, D, int(rng.integers(1, 3)), int(rng.integers(1, 14)),
+                      transpose))
+    return cases
+
+
+RANDOM_PERMUTE = _random_permute_cases()
+
+
+@pytest.mark.parametrize("name,grid,tile,dtype,D,batch,heads,transpose", RANDOM_PERMUTE,
+                         ids=[c[0] for c in RANDOM_PERMUTE])
+def test_permute_random_shapes(na, name, grid, tile, dtype, D, batch, heads, transpose):
+    # seeded random grids, power-of-two tiles of 1 .. 256 tokens, head dims,
+    # head counts and element sizes: the tile layout bit for bit against the
+    # NumPy index computation, and the round trip
+    say(f"[permute] random {name} grid={grid} tile={tile} {dtype} D={D} B={batch} heads={heads} "
+        f"transpose={transpose}")
+    g = torch.Generator("cpu").manual_seed(3100 + int(name[1:]))
+    x = torch.randn((batch, *grid, heads, D), generator=g).to(dtype)
+    if transpose and math.prod(tile) * (D * x.element_size() + 4) > 65536:
+        with pytest.raises(na.NAError):   # the staged tile would not fit in 64 KiB of LDS: refused on the host
+            na.permute(x.cuda(), tile, transpose=True)
+        return
+    xt = na.permute(x.cuda(), tile, transpose=transpose)
+    torch.cuda.synchronize()
+    ib = {torch.bfloat16: torch.int16, torch.float32: torch.int32, torch.float8_e4m3fn: torch.uint8}[dtype]
+    ref = _ref_tile_order(x.view(ib).numpy(), tile, transpose)
+    assert np.array_equal(xt.cpu().view(ib).numpy(), ref)
+    if not transpose:
+        back = na.unpermute(xt, grid, tile)
+        torch.cuda.synchronize()
+        assert torch.equal(back.cpu().view(ib), x.view(ib))
