@@ -390,8 +390,8 @@ size_t na_backward_workspace_bytes(int batch, int heads, int head_dim,
  *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
  *   dv_j = sum_i p_ij dout_i
  * over exactly the forward's (query, key) pairs.  bf16 with head_dim 64 or
- * 128 only (else NA_ERR_UNSUPPORTED); the grid must admit 128-token Q and KV
- * tiles at least 8 wide along W (W extent >= 5).
+ * 128 only (else NA_ERR_UNSUPPORTED).  It runs on 128-token Q and KV tiles
+ * at least 8 wide along W (padded to 8 when the grid is narrower).
  *
  * q, k, v  device, the forward's inputs, [batch, T, H, W, heads, head_dim].
  * out, lse device, the forward's outputs for these inputs (out bf16 as
@@ -429,6 +429,10 @@ na_status na_backward(const void* q, const void* k, const void* v,
  * Every call on one GPU shares that GPU's buffer, which keeps the last
  * call's contents: calls that overlap on one GPU (different streams, no
  * ordering between them) race and may produce wrong results.
+ * After a first call for a geometry on a device (which builds the host map
+ * and looks up the buffer's address), a call may be captured into a HIP
+ * graph: the capture holds the map copy and the kernel, so each replay
+ * rewrites the buffer before using it.
  * Arguments, layouts and other errors as for na_forward. */
 na_status na_forward_noalloc(const void* q, const void* k, const void* v,
                              void* out, float* lse, int batch, int heads,

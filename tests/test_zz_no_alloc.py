@@ -76,3 +76,40 @@ def test_noalloc_random_geometries_in_a_row(na):
         _noalloc(na, wl, q, k, v, out, lse)
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+def test_noalloc_replays_in_hip_graphs(na):
+    # the callers it is for include code under graph capture: after a first
+    # eager call per geometry, each call is a host-to-device copy of the tile
+    # map into the fixed buffer plus the kernel, both captured.  Two graphs of
+    # different geometries replayed alternately (each rewrites the shared
+    # buffer before its kernel), outputs poisoned by eager work in between:
+    # every replay equals the eager result bit for bit.
+    wls = [WORKLOADS["video_block"].with_(name="g1", grid=(8, 16, 24), window=(6, 8, 8), stride=(4, 4, 4), heads=2,
+                                          seed=311),
+           WORKLOADS["video_sliding"].with_(name="g2", batch=1, heads=2, grid=(5, 19, 27), window=(3, 7, 9),
+                                            stride=(1, 2, 3), head_dim=64, seed=312)]
+    st = []
+    for wl in wls:
+        qc, kc, vc, _ = make_qkv(wl, device="cpu")
+        q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+        _noalloc(na, wl, q, k, v, out, lse)
+        torch.cuda.synchronize()
+        st.append((wl, q, k, v, out, lse, out.clone(), lse.clone()))
+    graphs = []
+    for wl, q, k, v, out, lse, _, _ in st:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            _noalloc(na, wl, q, k, v, out, lse)
+        graphs.append(g)
+    for rep in range(3):
+        for g, (wl, q, k, v, out, lse, out_e, lse_e) in zip(graphs, st):
+            say(f"[noalloc] graph replay {rep} {wl.name}")
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, out_e) and torch.equal(lse, lse_e)
