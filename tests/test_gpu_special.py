@@ -445,3 +445,39 @@ def test_permute_random_shapes(na, name, grid, tile, dtype, D, batch, heads, tra
         back = na.unpermute(xt, grid, tile)
         torch.cuda.synchronize()
         assert torch.equal(back.cpu().view(ib), x.view(ib))
+
+
+def test_calls_on_a_side_stream(na, path):
+    # every call takes the caller's stream: the first call of a new geometry
+    # (plan built and uploaded) and later ones on a non-default stream give
+    # the default stream's results bit for bit, for the forward (each form),
+    # and in form 1 for the backward and the top-k forward too
+    import gpu_util
+    wl = WORKLOADS["video_sliding"].with_(batch=2, heads=3, grid=(6, 13, 21), window=(3, 5, 9), stride=(1, 2, 4),
+                                          seed=4242 + len(path))
+    say(f"[special] side stream ({path})")
+    _, _, _, _, q, k, v = inputs(wl)
+    ws = gpu_util.USE_WORKSPACE
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o1, l1 = na.forward(q, k, v, wl.window, wl.stride, scale=wl.scale, stream=side, workspace=ws)
+        o1b, l1b = na.forward(q, k, v, wl.window, wl.stride, scale=wl.scale, stream=side, workspace=ws)
+    side.synchronize()
+    o2, l2 = na.forward(q, k, v, wl.window, wl.stride, scale=wl.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2) and torch.equal(o1b, o2) and torch.equal(l1b, l2)
+    if path != "qo":
+        return
+    g = torch.Generator("cpu").manual_seed(4243)
+    do = torch.randn(q.shape, generator=g).to(torch.bfloat16).cuda()
+    with torch.cuda.stream(side):
+        side.wait_stream(torch.cuda.default_stream())
+        g1 = na.backward(q, k, v, o2, l2, do, wl.window, wl.stride, scale=wl.scale, stream=side)
+        t1 = na.topk_forward(q, k, v, 3, scale=wl.scale, stream=side)
+    side.synchronize()
+    g2 = na.backward(q, k, v, o2, l2, do, wl.window, wl.stride, scale=wl.scale)
+    t2 = na.topk_forward(q, k, v, 3, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+    assert all(torch.equal(a, b) for a, b in zip(t1, t2))
